@@ -1,0 +1,101 @@
+"""Geometry of the synthetic engram workloads.
+
+Each workload fixes the hash geometry (vocabulary, compressed id space, n-gram
+size, heads, layers, prime range), the table format, the projection shape and
+the token stream.  Sizes follow the DeepSeek-V4.1 Flash engram as the
+atlascybernetics page "spark_model/layers/engram_v41.rs" describes it (module
+doc: four stages; `EngramV41::new`: hc in 1..=4; `ENGRAM_ROW_BYTES`: one 84-byte
+Q2_K block per 256-wide row) and the metrale page
+"metrale_model_arch/deepseek_v41_ref/engram.rs" (`EngramTables`: fp8 e4m3 rows
+with power-of-two scales per `scale_block` values).
+
+No arithmetic of the method lives here: only shapes and distributions.
+"""
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    # table family: workloads that share hash tables, tables and weights
+    # share a family id (the prefill workload reuses the decode tables)
+    family: int
+    vocab: int
+    compressed: int          # size of the compressed id space
+    p_unmapped: float        # probability that a vocab id maps to -1
+    max_ngram: int
+    n_heads: int
+    n_layers: int
+    prime_lo: int            # primes drawn distinct from [prime_lo, prime_hi]
+    prime_hi: int
+    fmt: str                 # "q2k" or "e4m3"
+    head_dim: int = 256
+    scale_block: int = 128   # e4m3 only: values per power-of-two scale
+    scale_k_lo: int = -4     # e4m3 only: scale = 2**k, k uniform in [lo, hi]
+    scale_k_hi: int = 0
+    dim: int = 4096
+    hc: int = 4
+    token_dist: str = "uniform"   # "uniform" or "zipf"
+    zipf_s: float = 1.1
+    # token stream: `prompt` tokens as one prefill call (in chunks of
+    # `chunk`), then `decode_steps` single-token steps
+    prompt: int = 64
+    chunk: int = 0           # 0 = one call for the whole prompt
+    decode_steps: int = 0
+    eps: float = 1e-6
+    wkv_std: float = 0.02
+    qk_std: float = 0.05     # q, k = bf16(1 + qk_std * N(0,1))
+    pad_id: int = 0
+
+    @property
+    def cols(self) -> int:
+        return (self.max_ngram - 1) * self.n_heads
+
+    @property
+    def K(self) -> int:
+        return self.cols * self.head_dim
+
+    @property
+    def N(self) -> int:
+        return self.dim * (self.hc + 1)
+
+    @property
+    def total_tokens(self) -> int:
+        return self.prompt + self.decode_steps
+
+    @property
+    def row_bytes(self) -> int:
+        if self.fmt == "q2k":
+            return 84
+        return self.head_dim + 4 * (self.head_dim // self.scale_block)
+
+
+TINY_E4M3 = Workload(
+    name="tiny_e4m3_T64", family=0, vocab=1024, compressed=800, p_unmapped=0.10,
+    max_ngram=3, n_heads=2, n_layers=1, prime_lo=500, prime_hi=1000, fmt="e4m3",
+    dim=256, hc=4, token_dist="uniform", prompt=64)
+
+DECODE_Q2K = Workload(
+    name="decode_q2k_2layer_T1", family=1, vocab=129280, compressed=100000,
+    p_unmapped=0.15, max_ngram=4, n_heads=8, n_layers=2, prime_lo=2**17,
+    prime_hi=2**18, fmt="q2k", token_dist="uniform", prompt=32, decode_steps=256)
+
+PREFILL_Q2K = replace(
+    DECODE_Q2K, name="prefill_q2k_2layer_T4096", token_dist="zipf", prompt=4096,
+    decode_steps=0)
+
+SPLIT_E4M3 = Workload(
+    name="split_e4m3_2layer_8192x2048_then_128", family=3, vocab=129280,
+    compressed=100000, p_unmapped=0.15, max_ngram=4, n_heads=8, n_layers=2,
+    prime_lo=2**17, prime_hi=2**18, fmt="e4m3", token_dist="zipf", prompt=8192,
+    chunk=2048, decode_steps=128)
+
+GATHER_Q2K = Workload(
+    name="gather_stress_q2k_1layer_T16384", family=4, vocab=129280,
+    compressed=100000, p_unmapped=0.15, max_ngram=4, n_heads=8, n_layers=1,
+    prime_lo=2**21, prime_hi=2**22, fmt="q2k", token_dist="uniform", prompt=16384)
+
+WORKLOADS = {w.name: w for w in (TINY_E4M3, DECODE_Q2K, PREFILL_Q2K, SPLIT_E4M3, GATHER_Q2K)}
+# seed index of each workload's token / highway stream (tables use `family`)
+STREAM_INDEX = {TINY_E4M3.name: 0, DECODE_Q2K.name: 1, PREFILL_Q2K.name: 2,
+                SPLIT_E4M3.name: 3, GATHER_Q2K.name: 4}
