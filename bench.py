@@ -1,0 +1,307 @@
+"""Engram hot-path benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Headline: the decode workload (two Q2_K engram layers, 32-token prompt, then
+single-token steps; wkv [20480, 6144] bf16 per layer).  One step = one token
+through both layers: hash, then per layer gather + dequant, projection (GEMV)
+and gate, all through engram_forward.  `value` = engram tokens/s per layer =
+steps * layers / seconds, inputs resident in HBM.
+
+Also measured in the same run: the prefill workload (T = 4096 Zipf tokens,
+both layers, one hash pass; projection on the MFMA GEMM), reported under
+"prefill" with its own roofline.
+
+Per-kernel durations come from HIP events recorded by the library on the
+forward's stream around each stage (engram_ctx_set_timing) during a second
+pass over the same steps; the plain pass gives `value`.  The roofline uses the
+projection kernel: algorithmic bytes (decode GEMV) or flops (prefill GEMM)
+per launch divided by its average event-timed duration.  `traffic` is read
+from the committed rocprofv3 counter summary when it matches the current
+kernel source, else null.
+
+The oracle (plain C on the host cores) is timed on a bounded sample of the
+same decode steps for `cpu_baseline`.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gram_hashed_embedding_engram_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(name):
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(summary, kernel_src):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current source of the kernel."""
+    path = os.path.join(PROFILE_DIR, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest(kernel_src):
+        return None
+    return float(t.group(1))
+
+
+def device_inputs(w, torch, E, G):
+    ht = G.hash_tables(w)
+    tm = torch.from_numpy(ht["token_map"]).cuda()
+    tables = E.HashTables(tm, ht["pad_id"], ht["multipliers"], ht["primes"], ht["offsets"])
+    layers = []
+    host = []
+    for l in range(w.n_layers):
+        L = G.layer_inputs(w, ht, l)
+        data = torch.from_numpy(L["table"]).cuda()
+        scales = None if L["scales"] is None else torch.from_numpy(L["scales"]).cuda()
+        tab = E.Table(data, scales, head_dim=w.head_dim, scale_block=w.scale_block)
+        wkv = torch.from_numpy(L["wkv"].view(np.int16)).cuda()
+        qk = torch.empty(w.hc, w.dim, dtype=torch.float32, device="cuda")
+        E.qk_product(torch.from_numpy(L["q"].view(np.int16)).cuda(),
+                     torch.from_numpy(L["k"].view(np.int16)).cuda(), qk)
+        layers.append((tab, wkv, qk))
+        host.append(L)
+    torch.cuda.synchronize()
+    return ht, tm, tables, layers, host
+
+
+def make_ctx(E, w, tables, layers, max_tokens, max_seq):
+    ctx = E.Context(tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
+    for l, (tab, wkv, qk) in enumerate(layers):
+        ctx.add_layer(l, tab, wkv, qk)
+    ctx.reset()
+    return ctx
+
+
+def bench_decode(args, torch, E, G, synth):
+    w = synth.DECODE_Q2K
+    log(f"decode: generating {w.name}")
+    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    n_tok = w.prompt + 2 * (args.warmup + args.steps)
+    ids = G.token_ids(w, n_tok)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    hw = torch.from_numpy(G.highway(w, w.decode_steps, decode=True)).cuda()
+    prompt_h = torch.from_numpy(G.highway(w, w.prompt)).cuda()
+    ctx = make_ctx(E, w, tables, layers, w.prompt, n_tok)
+    stream = torch.cuda.current_stream()
+    nl = w.n_layers
+    for l in range(nl):
+        ctx.forward(l, d_ids[:w.prompt], w.prompt, prompt_h)
+    pos = w.prompt
+
+    def step(i):
+        nonlocal pos
+        h = hw[i % w.decode_steps:i % w.decode_steps + 1]
+        for l in range(nl):
+            ctx.forward(l, d_ids[pos:pos + 1], 1, h)
+        pos += 1
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    # second pass over the same number of steps with per-stage events
+    ctx.set_timing(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = ctx.timing()
+    ctx.set_timing(False)
+    ctx.check()
+    K, N = w.K, w.N
+    gemv_bytes = N * K * 2 + K * 2 + N * 2
+    gemv_ms, gemv_n = stages["project"]
+    gemv_avg = gemv_ms / gemv_n
+    gather_ms, gather_n = stages["gather"]
+    gather_bytes = w.cols * (84 + 512 + 8)
+    res = dict(
+        ms_per_step=ms / args.steps,
+        value=args.steps * nl / (ms / 1e3),
+        gemv_avg_ms=gemv_avg,
+        gemv_bytes=gemv_bytes,
+        stages={k: v[0] / max(1, v[1]) for k, v in stages.items()},
+        gather_GBps=gather_bytes / (gather_ms / gather_n / 1e3) / 1e9,
+        host=host, ht=ht, ids=ids,
+    )
+    del ctx
+    return res
+
+
+def bench_prefill(args, torch, E, G, synth):
+    w = synth.PREFILL_Q2K
+    log(f"prefill: generating {w.name}")
+    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    T = w.prompt
+    reps = args.prefill_steps
+    warm = 2
+    ids = G.token_ids(w)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    h = torch.from_numpy(G.highway(w, T)).cuda()
+    ctx = make_ctx(E, w, tables, layers, T, T * (warm + 2 * reps))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(w.n_layers):
+            ctx.forward(l, d_ids, T, h)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ctx.set_timing(True)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    stages = ctx.timing()
+    ctx.check()
+    flops = 2.0 * T * w.K * w.N
+    gemm_ms = stages["project"][0] / stages["project"][1]
+    gather_ms = stages["gather"][0] / stages["gather"][1]
+    gate_ms = stages["gate"][0] / stages["gate"][1]
+    tflops = flops / (gemm_ms / 1e3) / 1e12
+    gate_bytes = T * w.hc * w.dim * 8 + T * w.N * 2
+    return dict(
+        workload=w.name, T=T, layers=w.n_layers,
+        ms_per_step=ms / reps,
+        value=reps * T * w.n_layers / (ms / 1e3),
+        unit="engram tokens/s per layer",
+        stages_ms={k: v[0] / max(1, v[1]) for k, v in stages.items()},
+        roofline=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=tflops / BF16_PEAK_TFLOPS,
+                      traffic=counter_traffic("gemm_prefill_T4096_counters.md", "gemm.hip")),
+        gather_GBps=T * w.cols * (84 + 512 + 8) / (gather_ms / 1e3) / 1e9,
+        gate_GBps=gate_bytes / (gate_ms / 1e3) / 1e9,
+    )
+
+
+def cpu_baseline(res, synth, budget_s):
+    """The oracle on the host cores over the first decode steps (both
+    layers), until budget_s seconds of work have run."""
+    import oracle
+    w = synth.DECODE_Q2K
+    ht, host, ids = res["ht"], res["host"], res["ids"]
+    threads = oracle.default_threads()
+    hasher = oracle.Hasher(ht["token_map"], ht["pad_id"], ht["multipliers"], ht["primes"],
+                           ht["offsets"], ids.size)
+    hasher.hash(ids[:w.prompt], 0)
+    h = np.random.default_rng(0).standard_normal((1, w.hc, w.dim)).astype(np.float32)
+    pos, steps = w.prompt, 0
+    t0 = time.perf_counter()
+    while True:
+        rid = hasher.hash(ids[pos:pos + 1], pos)
+        for l in range(w.n_layers):
+            L = host[l]
+            rows = oracle.gather(L["table"], None, rid[:, l, :]).reshape(1, -1)
+            kv = oracle.linear_bf16(rows, L["wkv"], nthreads=threads)
+            h = oracle.gate_and_add(h, kv, L["q"], L["k"], w.eps, nthreads=1)
+        pos += 1
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 256:
+            break
+    return dict(value=steps * w.n_layers / el, unit="engram tokens/s per layer", cores=threads,
+                kind="oracle",
+                sample=f"the first {steps} decode steps of {w.name} (both layers: hash, "
+                       f"gather, projection, gate), {el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the engram path here runs on a single MI355X "
+              "(no sharded or multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gram_hashed_embedding_engram_amd as E
+    import synth
+    from synth import generate as G
+    E.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dec = bench_decode(args, torch, E, G, synth)
+    log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
+    pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
+    if pre:
+        log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host cores")
+        cpu = cpu_baseline(dec, synth, args.cpu_budget)
+    w = synth.DECODE_Q2K
+    gbps = dec["gemv_bytes"] / (dec["gemv_avg_ms"] / 1e3) / 1e9
+    out = {
+        "metric": "engram tokens/s per layer (decode T=1)",
+        "value": dec["value"],
+        "unit": "engram tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; the pages publish no throughput to compare)",
+        "config": {"workload": w.name, "layers": w.n_layers, "tokens_per_step": 1,
+                   "prompt": w.prompt, "table": "q2k", "rows_per_layer": int(
+                       dec["ht"]["rows"][0]), "K": w.K, "N": w.N, "hc": w.hc, "dim": w.dim},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": counter_traffic("gemv_decode_counters.md", "gemv.hip"),
+                     "kernel": "gemv_kernel<1,12> (projection, one launch per layer-step)",
+                     "bytes_per_launch": dec["gemv_bytes"], "avg_launch_ms": dec["gemv_avg_ms"]},
+        "stages_ms_per_layer_step": dec["stages"],
+        "gather_GBps": dec["gather_GBps"],
+        "prefill": pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,271 @@
+"""Python binding of libengram.so, the gfx950 engram hot path.
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of the path runs in the library's kernels.
+The names follow the C ABI in include/engram.h.  There is no fallback: if
+the library is not built, every call raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libengram.so")
+
+OK = 0
+E_ARG, E_RANGE, E_UNSUPPORTED, E_STATE, E_HIP, E_DEVICE = -1, -2, -3, -4, -5, -6
+DEVERR_TOKEN, DEVERR_ROW = 1, 2
+FMT_Q2K, FMT_E4M3 = 0, 1
+Q2K_ROW_BYTES = 84
+STAGES = ("hash", "gather", "project", "gate")
+
+# Every symbol include/engram.h declares.
+EXPORTS = (
+    "engram_last_error", "engram_abi_version", "engram_hash", "engram_gather_dequant",
+    "engram_project", "engram_qk_product", "engram_gate_apply", "engram_workspace_bytes",
+    "engram_ctx_create", "engram_ctx_add_layer", "engram_reset", "engram_forward",
+    "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_timing",
+    "engram_ctx_timing", "engram_ctx_destroy",
+)
+
+
+class EngramError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"engram error {code}: {msg}")
+        self.code = code
+
+
+class HashTablesC(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("max_ngram", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("vocab", ctypes.c_int64), ("pad_id", ctypes.c_int64),
+                ("d_token_map", ctypes.c_void_p), ("multipliers", ctypes.c_void_p),
+                ("primes", ctypes.c_void_p), ("offsets", ctypes.c_void_p)]
+
+
+class TableC(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_rows", ctypes.c_int64), ("d_data", ctypes.c_void_p),
+                ("d_scales", ctypes.c_void_p)]
+
+
+class ConfigC(ctypes.Structure):
+    _fields_ = [("hc", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dim", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64), ("max_seq", ctypes.c_int64),
+                ("hash", HashTablesC)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libengram.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(the engram path has no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        sig = {
+            "engram_last_error": (ctypes.c_char_p, []),
+            "engram_abi_version": (i32, []),
+            "engram_hash": (i32, [p, p, i64, i64, p, i64, p, p, p]),
+            "engram_gather_dequant": (i32, [p, p, i64, i32, i64, p, p, p]),
+            "engram_project": (i32, [p, p, p, i64, i64, i64, p]),
+            "engram_qk_product": (i32, [p, p, p, i64, p]),
+            "engram_gate_apply": (i32, [p, p, p, i64, i32, i64, ctypes.c_float, p]),
+            "engram_workspace_bytes": (ctypes.c_size_t, [p]),
+            "engram_ctx_create": (i32, [p, p, ctypes.c_size_t, p]),
+            "engram_ctx_add_layer": (i32, [p, i32, p, p, p]),
+            "engram_reset": (i32, [p, p]),
+            "engram_forward": (i32, [p, i32, p, i64, p, p]),
+            "engram_check": (i32, [p, p]),
+            "engram_position": (i64, [p]),
+            "engram_ctx_buffers": (i32, [p, p, p, p, p]),
+            "engram_ctx_set_timing": (i32, [p, i32]),
+            "engram_ctx_timing": (i32, [p, p, p]),
+            "engram_ctx_destroy": (None, [p]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().engram_last_error().decode()
+
+
+def _check(rc):
+    if rc != OK:
+        raise EngramError(rc, last_error())
+
+
+def _ptr(t):
+    """Device (or host numpy) address of a tensor / array; None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class HashTables:
+    """Hash tables for the ABI: token_map on the device (torch int64
+    tensor), multipliers / primes / offsets as host arrays."""
+
+    def __init__(self, d_token_map, pad_id, multipliers, primes, offsets):
+        self.mult = np.ascontiguousarray(multipliers, dtype=np.int64)
+        self.primes = np.ascontiguousarray(primes, dtype=np.int64)
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.token_map = d_token_map
+        self.n_layers, self.max_ngram = self.mult.shape
+        self.cols = self.primes.shape[1]
+        self.n_heads = self.cols // (self.max_ngram - 1)
+        self.c = HashTablesC(self.n_layers, self.max_ngram, self.n_heads, 0,
+                             int(d_token_map.numel()), int(pad_id), _ptr(d_token_map),
+                             self.mult.ctypes.data, self.primes.ctypes.data,
+                             self.offsets.ctypes.data)
+
+
+class Table:
+    """One layer's device-resident table (Q2_K blocks, or e4m3 codes with
+    f32 block scales)."""
+
+    def __init__(self, d_data, d_scales=None, head_dim=256, scale_block=128):
+        fmt = FMT_Q2K if d_scales is None else FMT_E4M3
+        n_rows = int(d_data.shape[0])
+        self.data, self.scales = d_data, d_scales
+        self.c = TableC(fmt, head_dim, scale_block if fmt == FMT_E4M3 else 0, 0, n_rows,
+                        _ptr(d_data), _ptr(d_scales))
+
+
+def hash(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err=None, stream=None):
+    _check(lib().engram_hash(ctypes.byref(tables.c), _ptr(d_ids), int(d_ids.numel()),
+                             int(start_pos), _ptr(d_history), int(d_history.numel()),
+                             _ptr(d_row_ids), _ptr(d_err), _stream(stream)))
+
+
+def gather_dequant(table: Table, d_row_ids, T, cols, id_stride, d_rows, d_err=None,
+                   stream=None):
+    _check(lib().engram_gather_dequant(ctypes.byref(table.c), _ptr(d_row_ids), int(T),
+                                       int(cols), int(id_stride), _ptr(d_rows), _ptr(d_err),
+                                       _stream(stream)))
+
+
+def project(d_x, d_w, d_y, stream=None):
+    T, K = d_x.shape
+    N = d_w.shape[0]
+    _check(lib().engram_project(_ptr(d_x), _ptr(d_w), _ptr(d_y), T, K, N, _stream(stream)))
+
+
+def qk_product(d_q, d_k, d_qk, stream=None):
+    _check(lib().engram_qk_product(_ptr(d_q), _ptr(d_k), _ptr(d_qk), int(d_q.numel()),
+                                   _stream(stream)))
+
+
+def gate_apply(d_h, d_kv, d_qk, eps, stream=None):
+    T, hc, dim = d_h.shape
+    _check(lib().engram_gate_apply(_ptr(d_h), _ptr(d_kv), _ptr(d_qk), T, hc, dim,
+                                   float(eps), _stream(stream)))
+
+
+class Context:
+    """The stateful engram of one sequence (engram_ctx)."""
+
+    def __init__(self, tables: HashTables, hc, dim, head_dim, eps, max_tokens, max_seq,
+                 d_workspace=None):
+        import torch
+        self.tables = tables
+        self.cfg = ConfigC(hc, head_dim, dim, eps, 0, max_tokens, max_seq, tables.c)
+        nbytes = lib().engram_workspace_bytes(ctypes.byref(self.cfg))
+        if nbytes == 0:
+            raise EngramError(E_ARG, "invalid engram configuration")
+        if d_workspace is None:
+            d_workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.workspace = d_workspace
+        self.nl, self.cols = tables.n_layers, tables.cols
+        self.hc, self.dim, self.head_dim = hc, dim, head_dim
+        h = ctypes.c_void_p()
+        _check(lib().engram_ctx_create(ctypes.byref(self.cfg), _ptr(d_workspace),
+                                       int(d_workspace.numel()), ctypes.byref(h)))
+        self.h = h
+        self._keep = {}
+
+    def add_layer(self, hash_index, table: Table, d_wkv, d_qk):
+        self._keep[hash_index] = (table, d_wkv, d_qk)
+        _check(lib().engram_ctx_add_layer(self.h, hash_index, ctypes.byref(table.c),
+                                          _ptr(d_wkv), _ptr(d_qk)))
+
+    def reset(self, stream=None):
+        _check(lib().engram_reset(self.h, _stream(stream)))
+
+    def forward(self, hash_index, d_ids, T, d_h, stream=None):
+        _check(lib().engram_forward(self.h, hash_index, _ptr(d_ids), int(T), _ptr(d_h),
+                                    _stream(stream)))
+
+    def check(self, stream=None):
+        _check(lib().engram_check(self.h, _stream(stream)))
+
+    @property
+    def position(self):
+        return lib().engram_position(self.h)
+
+    def buffers(self):
+        """(row_ids, rows, kv, err) device addresses."""
+        ptrs = [ctypes.c_void_p() for _ in range(4)]
+        _check(lib().engram_ctx_buffers(self.h, *[ctypes.byref(q) for q in ptrs]))
+        return tuple(q.value for q in ptrs)
+
+    def views(self, T):
+        """torch views of the workspace: row ids [T, nl, cols] int64, rows
+        [T, cols*head_dim] bf16 bits (int16), kv [T, dim*(hc+1)] (int16)."""
+        import torch
+        ws = self.workspace
+        base = ws.data_ptr()
+        rid, rows, kv, _ = self.buffers()
+
+        def view(addr, n, dtype, shape):
+            size = torch.empty(0, dtype=dtype).element_size()
+            off = addr - base
+            return ws[off:off + n * size].view(dtype).view(*shape)
+
+        K, N = self.cols * self.head_dim, self.dim * (self.hc + 1)
+        return (view(rid, T * self.nl * self.cols, torch.int64, (T, self.nl, self.cols)),
+                view(rows, T * K, torch.int16, (T, K)),
+                view(kv, T * N, torch.int16, (T, N)))
+
+    def set_timing(self, on: bool):
+        _check(lib().engram_ctx_set_timing(self.h, 1 if on else 0))
+
+    def timing(self):
+        ms = (ctypes.c_double * 4)()
+        n = (ctypes.c_int64 * 4)()
+        _check(lib().engram_ctx_timing(self.h, ms, n))
+        return {STAGES[i]: (ms[i], n[i]) for i in range(4)}
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().engram_ctx_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

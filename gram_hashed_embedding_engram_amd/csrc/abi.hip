@@ -1,0 +1,558 @@
+// The C ABI (include/engram.h): host-side validation, the stateful context
+// and dispatch to the kernels.  Every check runs before any launch, so a
+// refused call enqueues nothing (metrale "engram_v41" module index,
+// invariants: refusals happen before any copy or launch).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace engram {
+
+static thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int32_t launch_status(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(ENGRAM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ENGRAM_OK;
+}
+
+namespace {
+
+#define CHECK(cond, code, ...)                                                               \
+    do {                                                                                     \
+        if (!(cond))                                                                         \
+            return fail(code, __VA_ARGS__);                                                  \
+    } while (0)
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+// Hash tables -> kernel constants (atlascybernetics "engram_v41.rs",
+// EngramHashTables::from_flat: geometry and array checks).
+int32_t make_consts(const engram_hash_tables *t, HashConsts *c)
+{
+    CHECK(t, ENGRAM_E_ARG, "engram hash tables: NULL");
+    CHECK(t->n_layers > 0 && t->max_ngram >= 2 && t->n_heads > 0, ENGRAM_E_ARG,
+          "engram geometry: %d layers, ngram %d, heads %d", t->n_layers, t->max_ngram,
+          t->n_heads);
+    CHECK(t->n_layers <= ENGRAM_MAX_LAYERS && t->max_ngram <= ENGRAM_MAX_NGRAM, ENGRAM_E_UNSUPPORTED,
+          "engram geometry: %d layers (max %d), ngram %d (max %d)", t->n_layers,
+          ENGRAM_MAX_LAYERS, t->max_ngram, ENGRAM_MAX_NGRAM);
+    const int64_t cols = (int64_t)(t->max_ngram - 1) * t->n_heads;
+    CHECK(cols * t->n_layers <= ENGRAM_MAX_SLOTS, ENGRAM_E_UNSUPPORTED,
+          "engram geometry: %lld hash slots exceed %d", (long long)(cols * t->n_layers),
+          ENGRAM_MAX_SLOTS);
+    CHECK(t->vocab > 0 && t->d_token_map, ENGRAM_E_ARG, "engram token_map: vocab %lld, ptr %p",
+          (long long)t->vocab, (const void *)t->d_token_map);
+    CHECK(t->multipliers && t->primes && t->offsets, ENGRAM_E_ARG,
+          "engram hash constants: NULL array");
+    std::memset(c, 0, sizeof *c);
+    c->nl = t->n_layers;
+    c->ng = t->max_ngram;
+    c->nh = t->n_heads;
+    c->cols = (int32_t)cols;
+    c->vocab = t->vocab;
+    c->pad_id = t->pad_id;
+    for (int64_t i = 0; i < (int64_t)t->n_layers * t->max_ngram; i++) {
+        CHECK(t->multipliers[i] >= 0, ENGRAM_E_ARG,
+              "engram.multipliers[%lld] = %lld is negative (the tables hold values that fit i64)",
+              (long long)i, (long long)t->multipliers[i]);
+        c->mult[i] = t->multipliers[i];
+    }
+    for (int64_t i = 0; i < t->n_layers * cols; i++) {
+        CHECK(t->primes[i] > 0, ENGRAM_E_ARG, "engram.primes[%lld] = %lld must be positive",
+              (long long)i, (long long)t->primes[i]);
+        CHECK(t->offsets[i] >= 0 && t->offsets[i] <= ((int64_t)1 << 62) - t->primes[i],
+              ENGRAM_E_ARG, "engram.offsets[%lld] = %lld out of range", (long long)i,
+              (long long)t->offsets[i]);
+        c->prime[i] = t->primes[i];
+        c->offset[i] = t->offsets[i];
+    }
+    return ENGRAM_OK;
+}
+
+int32_t check_table(const engram_table *tab)
+{
+    CHECK(tab, ENGRAM_E_ARG, "engram table: NULL");
+    CHECK(tab->n_rows > 0 && tab->d_data, ENGRAM_E_ARG, "engram table: %lld rows, data %p",
+          (long long)tab->n_rows, (const void *)tab->d_data);
+    if (tab->fmt == ENGRAM_FMT_Q2K) {
+        CHECK(tab->head_dim == 256, ENGRAM_E_UNSUPPORTED,
+              "engram rows are one Q2_K block: head_dim must be 256, got %d", tab->head_dim);
+        CHECK(aligned(tab->d_data, 4), ENGRAM_E_ARG, "engram Q2_K table must be 4-byte aligned");
+    } else if (tab->fmt == ENGRAM_FMT_E4M3) {
+        CHECK(tab->head_dim >= 16 && tab->head_dim <= 1024 && tab->head_dim % 16 == 0,
+              ENGRAM_E_UNSUPPORTED, "engram e4m3 head_dim %d: a multiple of 16 up to 1024",
+              tab->head_dim);
+        CHECK(tab->scale_block >= 16 && tab->scale_block % 16 == 0 &&
+                  tab->head_dim % tab->scale_block == 0,
+              ENGRAM_E_UNSUPPORTED, "engram e4m3 scale_block %d must be a multiple of 16 dividing %d",
+              tab->scale_block, tab->head_dim);
+        CHECK(tab->d_scales, ENGRAM_E_ARG, "engram e4m3 table: NULL scales");
+        CHECK(aligned(tab->d_data, 16) && aligned(tab->d_scales, 4), ENGRAM_E_ARG,
+              "engram e4m3 table: codes must be 16-byte and scales 4-byte aligned");
+    } else {
+        return fail(ENGRAM_E_UNSUPPORTED, "engram table format %d", tab->fmt);
+    }
+    return ENGRAM_OK;
+}
+
+int32_t check_project(const uint16_t *x, const uint16_t *w, const uint16_t *y, int64_t T,
+                      int64_t K, int64_t N)
+{
+    CHECK(T >= 0, ENGRAM_E_ARG, "engram project: T = %lld", (long long)T);
+    CHECK(K >= 64 && K % 64 == 0, ENGRAM_E_UNSUPPORTED,
+          "engram project: K = %lld must be a positive multiple of 64", (long long)K);
+    CHECK(N >= 16 && N % 16 == 0, ENGRAM_E_UNSUPPORTED,
+          "engram project: N = %lld must be a positive multiple of 16", (long long)N);
+    CHECK(T * K < kMaxElems && N * K < kMaxElems && T * N < ((int64_t)1 << 40), ENGRAM_E_UNSUPPORTED,
+          "engram project: operands of %lld x %lld x %lld exceed 2^31 elements", (long long)T,
+          (long long)K, (long long)N);
+    CHECK(x && w && y, ENGRAM_E_ARG, "engram project: NULL pointer");
+    CHECK(aligned(x, 16) && aligned(w, 16) && aligned(y, 16), ENGRAM_E_ARG,
+          "engram project: x, w, y must be 16-byte aligned");
+    return ENGRAM_OK;
+}
+
+int32_t dispatch_project(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
+                         int64_t N, hipStream_t s)
+{
+    if (T == 0)
+        return ENGRAM_OK;
+    if (T <= kGemvMaxT && K <= kGemvMaxK)
+        return launch_gemv(x, w, y, T, K, N, s);
+    return launch_gemm(x, w, y, T, K, N, s);
+}
+
+int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
+                   int64_t dim, float eps)
+{
+    CHECK(T >= 0, ENGRAM_E_ARG, "engram gate: T = %lld", (long long)T);
+    CHECK(hc >= 1 && hc <= 4, ENGRAM_E_UNSUPPORTED, "engram gate supports hc_mult 1..=4, got %d",
+          hc);
+    CHECK(dim >= 256 && dim % 256 == 0 && dim <= (1 << 20), ENGRAM_E_UNSUPPORTED,
+          "engram gate: dim = %lld must be a multiple of 256", (long long)dim);
+    CHECK(std::isfinite(eps) && eps >= 0.0f, ENGRAM_E_ARG, "engram gate: eps = %g", (double)eps);
+    CHECK(h && kv && qk, ENGRAM_E_ARG, "engram gate: NULL pointer");
+    CHECK(aligned(h, 16) && aligned(kv, 8) && aligned(qk, 16), ENGRAM_E_ARG,
+          "engram gate: h and qk must be 16-byte, kv 8-byte aligned");
+    return ENGRAM_OK;
+}
+
+}  // namespace
+}  // namespace engram
+
+using namespace engram;
+
+// ------------------------------------------------------------ the context
+
+struct TimingRec {
+    int stage;
+    hipEvent_t a, b;
+};
+
+struct engram_ctx {
+    engram_config cfg;
+    HashConsts consts;
+    int32_t nl = 0, cols = 0;
+    int64_t kv_width = 0;
+    // workspace views
+    int64_t *history = nullptr, *row_ids = nullptr;
+    uint16_t *rows = nullptr, *kv = nullptr;
+    int32_t *err = nullptr;
+    struct Layer {
+        bool set = false;
+        engram_table tab{};
+        const uint16_t *wkv = nullptr;
+        const float *qk = nullptr;
+    } layers[ENGRAM_MAX_LAYERS];
+    int64_t pos = 0;
+    bool step_open = false;
+    int64_t step_T = 0;
+    bool timing = false;
+    std::vector<TimingRec> recs;
+    std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+struct Carve {
+    size_t history, row_ids, rows, kv, err, total;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool carve(const engram_config *cfg, Carve *c)
+{
+    if (!cfg || cfg->max_tokens <= 0 || cfg->max_seq <= 0 || cfg->dim <= 0 || cfg->hc <= 0 ||
+        cfg->head_dim <= 0 || cfg->hash.n_layers <= 0 || cfg->hash.max_ngram < 2 ||
+        cfg->hash.n_heads <= 0)
+        return false;
+    const int64_t cols = (int64_t)(cfg->hash.max_ngram - 1) * cfg->hash.n_heads;
+    size_t off = 0;
+    c->history = off;
+    off += round256(sizeof(int64_t) * (size_t)cfg->max_seq);
+    c->row_ids = off;
+    off += round256(sizeof(int64_t) * (size_t)(cfg->max_tokens * cfg->hash.n_layers * cols));
+    c->rows = off;
+    off += round256(2 * (size_t)(cfg->max_tokens * cols * cfg->head_dim));
+    c->kv = off;
+    off += round256(2 * (size_t)(cfg->max_tokens * cfg->dim * (cfg->hc + 1)));
+    c->err = off;
+    off += 256;
+    c->total = off;
+    return true;
+}
+
+hipEvent_t take_event(engram_ctx *ctx)
+{
+    if (!ctx->pool.empty()) {
+        hipEvent_t e = ctx->pool.back();
+        ctx->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+// Runs one stage's launch, bracketed by events when timing is on.
+template <class F>
+int32_t staged(engram_ctx *ctx, int stage, hipStream_t s, F &&launch)
+{
+    if (!ctx->timing)
+        return launch();
+    hipEvent_t a = take_event(ctx), b = take_event(ctx);
+    if (!a || !b)
+        return fail(ENGRAM_E_HIP, "engram timing: hipEventCreate failed");
+    (void)hipEventRecord(a, s);
+    const int32_t rc = launch();
+    (void)hipEventRecord(b, s);
+    ctx->recs.push_back({stage, a, b});
+    return rc;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ entry points
+
+extern "C" {
+
+const char *engram_last_error(void) { return g_last_error.c_str(); }
+
+int32_t engram_abi_version(void) { return ENGRAM_ABI_VERSION; }
+
+int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int64_t T,
+                    int64_t start_pos, int64_t *d_history, int64_t max_seq, int64_t *d_row_ids,
+                    int32_t *d_err, void *stream)
+{
+    HashConsts c;
+    int32_t rc = make_consts(tables, &c);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
+          "engram hash: T %lld, start_pos %lld, max_seq %lld", (long long)T,
+          (long long)start_pos, (long long)max_seq);
+    CHECK(start_pos + T <= max_seq, ENGRAM_E_RANGE, "engram hasher: %lld positions, %lld needed",
+          (long long)max_seq, (long long)(start_pos + T));
+    if (T == 0)
+        return ENGRAM_OK;
+    CHECK(d_ids && d_history && d_row_ids, ENGRAM_E_ARG, "engram hash: NULL pointer");
+    return launch_hash(c, tables->d_token_map, d_ids, T, start_pos, d_history, d_row_ids, d_err,
+                       as_stream(stream));
+}
+
+int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_ids, int64_t T,
+                              int32_t cols, int64_t id_stride, uint16_t *d_rows, int32_t *d_err,
+                              void *stream)
+{
+    int32_t rc = check_table(table);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(T >= 0 && cols >= 1 && id_stride >= cols, ENGRAM_E_ARG,
+          "engram gather: T %lld, cols %d, id_stride %lld", (long long)T, cols,
+          (long long)id_stride);
+    if (T == 0)
+        return ENGRAM_OK;
+    CHECK(d_row_ids && d_rows, ENGRAM_E_ARG, "engram gather: NULL pointer");
+    CHECK(aligned(d_rows, 16) && aligned(d_row_ids, 8), ENGRAM_E_ARG,
+          "engram gather: rows must be 16-byte, ids 8-byte aligned");
+    return launch_gather(*table, d_row_ids, T, cols, id_stride, d_rows, d_err, as_stream(stream));
+}
+
+int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
+                       int64_t K, int64_t N, void *stream)
+{
+    int32_t rc = check_project(d_x, d_w, d_y, T, K, N);
+    if (rc != ENGRAM_OK)
+        return rc;
+    return dispatch_project(d_x, d_w, d_y, T, K, N, as_stream(stream));
+}
+
+int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk, int64_t n,
+                          void *stream)
+{
+    CHECK(n >= 0, ENGRAM_E_ARG, "engram qk: n = %lld", (long long)n);
+    if (n == 0)
+        return ENGRAM_OK;
+    CHECK(d_q && d_k && d_qk, ENGRAM_E_ARG, "engram qk: NULL pointer");
+    return launch_qk_product(d_q, d_k, d_qk, n, as_stream(stream));
+}
+
+int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, int64_t T,
+                          int32_t hc, int64_t dim, float eps, void *stream)
+{
+    int32_t rc = check_gate(d_h, d_kv, d_qk, T, hc, dim, eps);
+    if (rc != ENGRAM_OK)
+        return rc;
+    return launch_gate(d_h, d_kv, d_qk, T, hc, dim, eps, as_stream(stream));
+}
+
+size_t engram_workspace_bytes(const engram_config *cfg)
+{
+    Carve c;
+    return carve(cfg, &c) ? c.total : 0;
+}
+
+int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t workspace_bytes,
+                          engram_ctx **out)
+{
+    CHECK(cfg && out, ENGRAM_E_ARG, "engram ctx: NULL config or output");
+    *out = nullptr;
+    HashConsts c;
+    int32_t rc = make_consts(&cfg->hash, &c);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(cfg->hc >= 1 && cfg->hc <= 4, ENGRAM_E_UNSUPPORTED,
+          "engram gate supports hc_mult 1..=4, got %d", cfg->hc);
+    CHECK(cfg->dim >= 256 && cfg->dim % 256 == 0, ENGRAM_E_UNSUPPORTED,
+          "engram dim %lld must be a multiple of 256", (long long)cfg->dim);
+    CHECK(cfg->head_dim >= 16 && cfg->head_dim % 16 == 0 && cfg->head_dim <= 1024,
+          ENGRAM_E_UNSUPPORTED, "engram head_dim %d", cfg->head_dim);
+    CHECK(std::isfinite(cfg->eps) && cfg->eps >= 0.0f, ENGRAM_E_ARG, "engram eps %g",
+          (double)cfg->eps);
+    CHECK(cfg->max_tokens >= 1 && cfg->max_seq >= 1, ENGRAM_E_ARG,
+          "engram ctx: max_tokens %lld, max_seq %lld", (long long)cfg->max_tokens,
+          (long long)cfg->max_seq);
+    const int64_t K = (int64_t)c.cols * cfg->head_dim, N = cfg->dim * (cfg->hc + 1);
+    CHECK(K % 64 == 0, ENGRAM_E_UNSUPPORTED, "engram ctx: cols*head_dim = %lld not a multiple of 64",
+          (long long)K);
+    CHECK(cfg->max_tokens * K < kMaxElems && N * K < kMaxElems, ENGRAM_E_UNSUPPORTED,
+          "engram ctx: projection operands exceed 2^31 elements");
+    Carve cv;
+    carve(cfg, &cv);
+    CHECK(d_workspace && aligned(d_workspace, 256), ENGRAM_E_ARG,
+          "engram ctx: workspace must be non-NULL and 256-byte aligned");
+    CHECK(workspace_bytes >= cv.total, ENGRAM_E_RANGE, "engram ctx: workspace %zu bytes, %zu needed",
+          workspace_bytes, cv.total);
+    engram_ctx *ctx = new engram_ctx();
+    ctx->cfg = *cfg;
+    ctx->cfg.hash.multipliers = ctx->cfg.hash.primes = ctx->cfg.hash.offsets = nullptr;
+    ctx->consts = c;
+    ctx->nl = c.nl;
+    ctx->cols = c.cols;
+    ctx->kv_width = N;
+    char *ws = (char *)d_workspace;
+    ctx->history = (int64_t *)(ws + cv.history);
+    ctx->row_ids = (int64_t *)(ws + cv.row_ids);
+    ctx->rows = (uint16_t *)(ws + cv.rows);
+    ctx->kv = (uint16_t *)(ws + cv.kv);
+    ctx->err = (int32_t *)(ws + cv.err);
+    *out = ctx;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_add_layer(engram_ctx *ctx, int32_t hash_index, const engram_table *table,
+                             const uint16_t *d_wkv, const float *d_qk)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram add_layer: NULL context");
+    CHECK(hash_index >= 0 && hash_index < ctx->nl, ENGRAM_E_ARG,
+          "engram add_layer: hash index %d outside 0..%d", hash_index, ctx->nl - 1);
+    int32_t rc = check_table(table);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(table->head_dim == ctx->cfg.head_dim, ENGRAM_E_ARG,
+          "engram add_layer: table head_dim %d, context %d", table->head_dim, ctx->cfg.head_dim);
+    int64_t need = 0;
+    for (int c = 0; c < ctx->cols; c++) {
+        const int slot = hash_index * ctx->cols + c;
+        const int64_t top = ctx->consts.offset[slot] + ctx->consts.prime[slot];
+        need = top > need ? top : need;
+    }
+    CHECK(table->n_rows >= need, ENGRAM_E_RANGE,
+          "engram add_layer: table has %lld rows, the hash reaches row %lld",
+          (long long)table->n_rows, (long long)need - 1);
+    CHECK(d_wkv && d_qk && aligned(d_wkv, 16) && aligned(d_qk, 16), ENGRAM_E_ARG,
+          "engram add_layer: wkv and qk must be non-NULL and 16-byte aligned");
+    engram_ctx::Layer &L = ctx->layers[hash_index];
+    L.set = true;
+    L.tab = *table;
+    L.wkv = d_wkv;
+    L.qk = d_qk;
+    return ENGRAM_OK;
+}
+
+int32_t engram_reset(engram_ctx *ctx, void *stream)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram reset: NULL context");
+    hipStream_t s = as_stream(stream);
+    int32_t rc = launch_fill_zero(ctx->history, sizeof(int64_t) * (size_t)ctx->cfg.max_seq, s);
+    if (rc == ENGRAM_OK)
+        rc = launch_fill_zero(ctx->err, 256, s);
+    if (rc != ENGRAM_OK)
+        return rc;
+    ctx->pos = 0;
+    ctx->step_open = false;
+    ctx->step_T = 0;
+    return ENGRAM_OK;
+}
+
+int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids, int64_t T,
+                       float *d_h, void *stream)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram forward: NULL context");
+    CHECK(hash_index >= 0 && hash_index < ctx->nl, ENGRAM_E_ARG,
+          "engram forward: hash index %d outside 0..%d", hash_index, ctx->nl - 1);
+    const engram_ctx::Layer &L = ctx->layers[hash_index];
+    CHECK(L.set, ENGRAM_E_STATE, "engram: layer %d has no weights", hash_index);
+    CHECK(T >= 1, ENGRAM_E_ARG, "engram forward: T = %lld", (long long)T);
+    CHECK(T <= ctx->cfg.max_tokens, ENGRAM_E_RANGE, "engram: %lld tokens exceed the %lld workspace",
+          (long long)T, (long long)ctx->cfg.max_tokens);
+    CHECK(d_h && aligned(d_h, 16), ENGRAM_E_ARG, "engram forward: highway NULL or misaligned");
+    if (hash_index == 0) {
+        CHECK(d_ids, ENGRAM_E_ARG, "engram forward: NULL token ids");
+        CHECK(ctx->pos + T <= ctx->cfg.max_seq, ENGRAM_E_RANGE,
+              "engram hasher: %lld positions, %lld needed", (long long)ctx->cfg.max_seq,
+              (long long)(ctx->pos + T));
+    } else {
+        CHECK(ctx->step_open, ENGRAM_E_STATE,
+              "engram forward: layer %d before layer 0 opened a step", hash_index);
+        CHECK(ctx->step_T == T, ENGRAM_E_STATE,
+              "engram forward: layer %d got %lld tokens, the step has %lld", hash_index,
+              (long long)T, (long long)ctx->step_T);
+    }
+    hipStream_t s = as_stream(stream);
+    const engram_config &cfg = ctx->cfg;
+    int32_t rc;
+    if (hash_index == 0) {
+        const int64_t start = ctx->pos;
+        rc = staged(ctx, 0, s, [&] {
+            return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, T, start, ctx->history,
+                               ctx->row_ids, ctx->err, s);
+        });
+        if (rc != ENGRAM_OK)
+            return rc;
+        ctx->pos += T;
+        ctx->step_open = true;
+        ctx->step_T = T;
+    }
+    const int64_t K = (int64_t)ctx->cols * cfg.head_dim;
+    rc = staged(ctx, 1, s, [&] {
+        return launch_gather(L.tab, ctx->row_ids + (int64_t)hash_index * ctx->cols, T, ctx->cols,
+                             (int64_t)ctx->nl * ctx->cols, ctx->rows, ctx->err, s);
+    });
+    if (rc != ENGRAM_OK)
+        return rc;
+    rc = staged(ctx, 2, s, [&] {
+        return dispatch_project(ctx->rows, L.wkv, ctx->kv, T, K, ctx->kv_width, s);
+    });
+    if (rc != ENGRAM_OK)
+        return rc;
+    return staged(ctx, 3, s, [&] {
+        return launch_gate(d_h, ctx->kv, L.qk, T, cfg.hc, cfg.dim, cfg.eps, s);
+    });
+}
+
+int32_t engram_check(engram_ctx *ctx, void *stream)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram check: NULL context");
+    hipError_t e = hipStreamSynchronize(as_stream(stream));
+    CHECK(e == hipSuccess, ENGRAM_E_HIP, "engram check: %s", hipGetErrorString(e));
+    int32_t word = 0;
+    e = hipMemcpy(&word, ctx->err, sizeof word, hipMemcpyDeviceToHost);
+    CHECK(e == hipSuccess, ENGRAM_E_HIP, "engram check: %s", hipGetErrorString(e));
+    CHECK(word == 0, ENGRAM_E_DEVICE, "engram device error 0x%x:%s%s", word,
+          (word & ENGRAM_DEVERR_TOKEN) ? " token id outside the vocabulary" : "",
+          (word & ENGRAM_DEVERR_ROW) ? " row id outside the table" : "");
+    return ENGRAM_OK;
+}
+
+int64_t engram_position(const engram_ctx *ctx) { return ctx ? ctx->pos : -1; }
+
+int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t **d_rows,
+                           uint16_t **d_kv, int32_t **d_err)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram buffers: NULL context");
+    if (d_row_ids)
+        *d_row_ids = ctx->row_ids;
+    if (d_rows)
+        *d_rows = ctx->rows;
+    if (d_kv)
+        *d_kv = ctx->kv;
+    if (d_err)
+        *d_err = ctx->err;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram timing: NULL context");
+    ctx->timing = enable != 0;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage, int64_t *launches_per_stage)
+{
+    CHECK(ctx && ms_per_stage && launches_per_stage, ENGRAM_E_ARG, "engram timing: NULL pointer");
+    for (int i = 0; i < 4; i++) {
+        ms_per_stage[i] = 0.0;
+        launches_per_stage[i] = 0;
+    }
+    int32_t rc = ENGRAM_OK;
+    for (const TimingRec &r : ctx->recs) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            rc = fail(ENGRAM_E_HIP, "engram timing: event query failed");
+        ms_per_stage[r.stage] += ms;
+        launches_per_stage[r.stage] += 1;
+        ctx->pool.push_back(r.a);
+        ctx->pool.push_back(r.b);
+    }
+    ctx->recs.clear();
+    return rc;
+}
+
+void engram_ctx_destroy(engram_ctx *ctx)
+{
+    if (!ctx)
+        return;
+    for (const TimingRec &r : ctx->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : ctx->pool)
+        (void)hipEventDestroy(e);
+    delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+// Stage 2: gather the hashed rows from an HBM-resident table and dequantise
+// them to bf16 (atlascybernetics "spark_model/layers/engram_v41.rs", module
+// doc stage 2 and rows_from_q2k; metrale "deepseek_v41_ref/engram.rs",
+// regen_table and embed_rows).
+//
+// Output row r = t*cols + c holds table row ids[t*id_stride + c]; the rows of
+// one token are contiguous, so the output is the [T, cols*head_dim] input of
+// the projection.
+//
+// Q2_K (84-byte blocks, only 4-byte aligned): a workgroup takes 64 rows at a
+// time.  It first stages the 64 blocks in LDS with one coalesced dword load
+// per (row, dword) -- 21 dwords a block -- spread over all 256 threads, then
+// each half-wave expands one row from LDS: lane i writes values 8i..8i+7 as
+// one 16-byte store, so a row leaves as one 512-byte coalesced write.
+//
+// Block layout (GGML k-quant; the pages give the size only): bytes 0..15
+// scale/min nibbles of the 16 sub-blocks of 16 values, bytes 16..79 the 2-bit
+// quants, bytes 80..83 fp16 d and dmin.  Value e uses quant byte
+// 32*(e/128) + e%32 at bit 2*((e%128)/32) and sub-block e/16; for lane i
+// (values 8i..8i+7) that is 8 consecutive quant bytes at 32*(i/16) + 8*(i%4),
+// shift 2*((i%16)/4), sub-block i/2.  y = d*scale*q - dmin*min: both products
+// are exact in f32, so the single subtraction and the bf16 rounding fix the
+// result bit for bit.
+//
+// e4m3 (16-byte aligned rows): a thread expands 16 codes of one row with one
+// 16-byte load and one scale, writing two 16-byte stores.  e4m3 times a
+// power-of-two scale is exact in bf16.
+#include "common.h"
+
+namespace engram {
+namespace {
+
+constexpr int kQ2kRows = 64;          // rows staged per workgroup iteration
+constexpr int kQ2kDwords = 21;        // 84 bytes
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__global__ __launch_bounds__(256) void gather_q2k_kernel(const uint8_t *__restrict__ table,
+                                                         int64_t n_table_rows,
+                                                         const int64_t *__restrict__ ids,
+                                                         int64_t id_stride, int32_t cols,
+                                                         int64_t total_rows,
+                                                         uint16_t *__restrict__ out,
+                                                         int32_t *__restrict__ err)
+{
+    __shared__ uint32_t blk[kQ2kRows * kQ2kDwords];
+    __shared__ int64_t row_off[kQ2kRows];
+    const int tid = threadIdx.x;
+
+    for (int64_t base = (int64_t)blockIdx.x * kQ2kRows; base < total_rows;
+         base += (int64_t)gridDim.x * kQ2kRows) {
+        if (tid < kQ2kRows) {
+            const int64_t r = base + tid;
+            int64_t off = -1;
+            if (r < total_rows) {
+                const int64_t t = r / cols;
+                const int64_t c = r - t * cols;
+                const int64_t id = ids[t * id_stride + c];
+                if (id >= 0 && id < n_table_rows)
+                    off = id * ENGRAM_Q2K_ROW_BYTES;
+                else if (err)
+                    atomicOr(err, ENGRAM_DEVERR_ROW);
+            }
+            row_off[tid] = off;
+        }
+        __syncthreads();
+        for (int w = tid; w < kQ2kRows * kQ2kDwords; w += 256) {
+            const int rr = w / kQ2kDwords;
+            const int d = w - rr * kQ2kDwords;
+            const int64_t off = row_off[rr];
+            blk[w] = off >= 0 ? *(const uint32_t *)(table + off + 4 * d) : 0u;
+        }
+        __syncthreads();
+
+        const int i = tid & 31;               // lane within the row: values 8i..8i+7
+        for (int rr = tid >> 5; rr < kQ2kRows; rr += 8) {
+            const int64_t r = base + rr;
+            if (r >= total_rows)
+                break;
+            const uint32_t *b = blk + rr * kQ2kDwords;
+            const uint32_t dd = b[20];
+            const float d = half_bits_to_f32(dd & 0xFFFFu);
+            const float dmin = half_bits_to_f32(dd >> 16);
+            const int sub = i >> 1;
+            const uint32_t sc = (b[sub >> 2] >> (8 * (sub & 3))) & 0xFFu;
+            const float dl = d * (float)(sc & 15u);
+            const float ml = dmin * (float)(sc >> 4);
+            const int qw = 4 + ((32 * (i >> 4) + 8 * (i & 3)) >> 2);   // dword of the 8 quants
+            const int shift = 2 * ((i & 15) >> 2);
+            const uint32_t q0 = b[qw] >> shift, q1 = b[qw + 1] >> shift;
+            float y[8];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                y[k] = dl * (float)((q0 >> (8 * k)) & 3u) - ml;
+                y[4 + k] = dl * (float)((q1 >> (8 * k)) & 3u) - ml;
+            }
+            uint4 o;
+            o.x = pack_bf16x2(y[0], y[1]);
+            o.y = pack_bf16x2(y[2], y[3]);
+            o.z = pack_bf16x2(y[4], y[5]);
+            o.w = pack_bf16x2(y[6], y[7]);
+            if (row_off[rr] < 0)
+                o = make_uint4(0, 0, 0, 0);
+            *(uint4 *)(out + r * 256 + 8 * i) = o;
+        }
+        __syncthreads();
+    }
+}
+
+// e4m3fn code -> f32, from the format: sign, 4 exponent bits (bias 7), 3
+// mantissa bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0)
+        return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
+    if (e == 15 && m == 7)
+        return __uint_as_float(0x7FC00000u | sign);
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+__global__ __launch_bounds__(256) void gather_e4m3_kernel(const uint8_t *__restrict__ codes,
+                                                          const float *__restrict__ scales,
+                                                          int64_t n_table_rows, int32_t head_dim,
+                                                          int32_t scale_block,
+                                                          const int64_t *__restrict__ ids,
+                                                          int64_t id_stride, int32_t cols,
+                                                          int64_t total_rows,
+                                                          uint16_t *__restrict__ out,
+                                                          int32_t *__restrict__ err)
+{
+    const int chunks = head_dim >> 4;      // 16 codes per thread
+    const int nb = head_dim / scale_block;
+    const int64_t total = total_rows * chunks;
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+         g += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = g / chunks;
+        const int ch = (int)(g - r * chunks);
+        const int64_t t = r / cols;
+        const int64_t c = r - t * cols;
+        const int64_t id = ids[t * id_stride + c];
+        uint4 o0 = make_uint4(0, 0, 0, 0), o1 = o0;
+        if (id >= 0 && id < n_table_rows) {
+            const uint4 v = *(const uint4 *)(codes + id * head_dim + 16 * ch);
+            const float s = scales[id * nb + (16 * ch) / scale_block];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t p[8];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                p[2 * k] = pack_bf16x2(e4m3_to_f32(w[k] & 0xFFu) * s,
+                                       e4m3_to_f32((w[k] >> 8) & 0xFFu) * s);
+                p[2 * k + 1] = pack_bf16x2(e4m3_to_f32((w[k] >> 16) & 0xFFu) * s,
+                                           e4m3_to_f32(w[k] >> 24) * s);
+            }
+            o0 = make_uint4(p[0], p[1], p[2], p[3]);
+            o1 = make_uint4(p[4], p[5], p[6], p[7]);
+        } else if (err && ch == 0) {
+            atomicOr(err, ENGRAM_DEVERR_ROW);
+        }
+        uint4 *dst = (uint4 *)(out + r * head_dim + 16 * ch);
+        dst[0] = o0;
+        dst[1] = o1;
+    }
+}
+
+}  // namespace
+
+int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T, int32_t cols,
+                      int64_t id_stride, uint16_t *rows, int32_t *err, hipStream_t s)
+{
+    const int64_t total_rows = T * cols;
+    if (total_rows == 0)
+        return ENGRAM_OK;
+    if (tab.fmt == ENGRAM_FMT_Q2K) {
+        int64_t blocks = (total_rows + kQ2kRows - 1) / kQ2kRows;
+        if (blocks > 16384)
+            blocks = 16384;
+        hipLaunchKernelGGL(gather_q2k_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tab.d_data,
+                           tab.n_rows, row_ids, id_stride, cols, total_rows, rows, err);
+    } else {
+        const int64_t threads = total_rows * (tab.head_dim / 16);
+        int64_t blocks = (threads + 255) / 256;
+        if (blocks > 16384)
+            blocks = 16384;
+        hipLaunchKernelGGL(gather_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           tab.d_data, tab.d_scales, tab.n_rows, tab.head_dim, tab.scale_block,
+                           row_ids, id_stride, cols, total_rows, rows, err);
+    }
+    return launch_status("engram gather kernel");
+}
+
+}  // namespace engram

@@ -1,0 +1,137 @@
+// Stage 3 at one to four tokens: the wkv projection as an HBM-streaming GEMV
+// (atlascybernetics "spark_model/layers/engram_v41.rs", EngramV41::gemv_k
+// and module doc stage 3; metrale "deepseek_v41_ref/engram.rs",
+// linear_bf16).  At a single token the projection reads every weight once
+// and does two flops per weight, so its bound is HBM bandwidth, not the
+// matrix cores.
+//
+// Layout: w [N][K] bf16, K contiguous.  One wavefront owns one output row at
+// a time and reads it as K/512 coalesced 1 KiB loads (16 bytes a lane, all
+// issued before the first is consumed, to keep many bytes in flight).  The
+// activations x [T][K] are loaded once per wave into registers, lane l
+// holding elements 8*(64*i + l) .. +7 of step i.  Waves are persistent and
+// take rows wave_id, wave_id + n_waves, ...  The per-lane f32 partial sums
+// are reduced across the wave; the sum is rounded once to bf16.
+#include "common.h"
+
+namespace engram {
+namespace {
+
+constexpr int kGemvBlocksPerCu = 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
+{
+    acc = fmaf(bf16_lo(w.x), bf16_lo(x.x), acc);
+    acc = fmaf(bf16_hi(w.x), bf16_hi(x.x), acc);
+    acc = fmaf(bf16_lo(w.y), bf16_lo(x.y), acc);
+    acc = fmaf(bf16_hi(w.y), bf16_hi(x.y), acc);
+    acc = fmaf(bf16_lo(w.z), bf16_lo(x.z), acc);
+    acc = fmaf(bf16_hi(w.z), bf16_hi(x.z), acc);
+    acc = fmaf(bf16_lo(w.w), bf16_lo(x.w), acc);
+    acc = fmaf(bf16_hi(w.w), bf16_hi(x.w), acc);
+    return acc;
+}
+
+template <int NT, int NI>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ w,
+                                                   uint16_t *__restrict__ y, int64_t K, int64_t N)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t kc = K >> 3;                       // 16-byte chunks per row
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 xr[NT][NI];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const u32x4 *xt = (const u32x4 *)(x + t * K);
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const int64_t idx = (int64_t)i * 64 + lane;
+            xr[t][i] = idx < kc ? xt[idx] : zero;
+        }
+    }
+
+    for (int64_t n = wave; n < N; n += n_waves) {
+        const u32x4 *wr = (const u32x4 *)(w + n * K);
+        u32x4 wv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const int64_t idx = (int64_t)i * 64 + lane;
+            wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
+        }
+        float acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            acc[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                acc[t] = dot8(wv[i], xr[t][i], acc[t]);
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const float s = wave_sum(acc[t]);
+            if (lane == t)
+                y[t * N + n] = f32_to_bf16(s);
+        }
+    }
+}
+
+template <int NT>
+int32_t launch_nt(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, int64_t N,
+                  hipStream_t s)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    const int64_t ni = (K + 511) / 512;
+    int64_t blocks = (N + 3) / 4;
+    const int64_t cap = (int64_t)cus * kGemvBlocksPerCu;
+    if (blocks > cap)
+        blocks = cap;
+    const dim3 grid((unsigned)blocks), block(256);
+#define ENGRAM_GEMV_CASE(NI_)                                                               \
+    case NI_:                                                                               \
+        hipLaunchKernelGGL((gemv_kernel<NT, NI_>), grid, block, 0, s, x, w, y, K, N);       \
+        break;
+    switch (ni) {
+        ENGRAM_GEMV_CASE(1) ENGRAM_GEMV_CASE(2) ENGRAM_GEMV_CASE(3) ENGRAM_GEMV_CASE(4)
+        ENGRAM_GEMV_CASE(5) ENGRAM_GEMV_CASE(6) ENGRAM_GEMV_CASE(7) ENGRAM_GEMV_CASE(8)
+        ENGRAM_GEMV_CASE(9) ENGRAM_GEMV_CASE(10) ENGRAM_GEMV_CASE(11) ENGRAM_GEMV_CASE(12)
+        ENGRAM_GEMV_CASE(13) ENGRAM_GEMV_CASE(14) ENGRAM_GEMV_CASE(15) ENGRAM_GEMV_CASE(16)
+    default:
+        return fail(ENGRAM_E_UNSUPPORTED, "engram gemv: K = %lld exceeds %lld", (long long)K,
+                    (long long)kGemvMaxK);
+    }
+#undef ENGRAM_GEMV_CASE
+    return launch_status("engram gemv kernel");
+}
+
+}  // namespace
+
+int32_t launch_gemv(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
+                    int64_t N, hipStream_t s)
+{
+    // two tokens share one pass over the weights; a third or fourth token
+    // takes another pass
+    for (int64_t t0 = 0; t0 < T; t0 += 2) {
+        const int64_t nt = T - t0 >= 2 ? 2 : 1;
+        const int32_t rc = nt == 2 ? launch_nt<2>(x + t0 * K, w, y + t0 * N, K, N, s)
+                                   : launch_nt<1>(x + t0 * K, w, y + t0 * N, K, N, s);
+        if (rc != ENGRAM_OK)
+            return rc;
+    }
+    return ENGRAM_OK;
+}
+
+}  // namespace engram

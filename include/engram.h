@@ -1,0 +1,269 @@
+/*
+ * engram.h -- C ABI of the MI355X (gfx950) engram hot path.
+ *
+ * The DeepSeek-V4.1 engram layer, per token: hash the n-gram window of
+ * compressed token ids into `cols` table row ids, gather and dequantise those
+ * rows to bf16, project their concatenation through `wkv` into one key per
+ * hyper-connection stream plus one shared value, and gate the value onto the
+ * FP32 highway (atlascybernetics "spark_model/layers/engram_v41.rs", module
+ * doc, stages 1-4; metrale "metrale_model_arch/deepseek_v41_ref/engram.rs",
+ * module doc).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* are device memory owned by the caller (this library
+ *     never allocates or frees device memory); every other pointer is host
+ *     memory, read during the call only.
+ *   - bf16 values travel as uint16_t bit patterns.  Arrays are row-major and
+ *     densely packed, with the shapes given in brackets.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work: they return before the GPU runs it and never synchronise,
+ *     except engram_check.
+ *   - Return value: ENGRAM_OK (0) or a negative ENGRAM_E_* code.  Every
+ *     argument check runs on the host before any launch; a refused call
+ *     enqueues nothing and leaves every buffer untouched.  engram_last_error()
+ *     returns the message of the calling thread's last failure.
+ *   - Errors only the device can see (a token id outside the vocabulary, a
+ *     row id outside the table) are recorded in a caller-supplied int32
+ *     error word (d_err, nullable) as a bit mask of ENGRAM_DEVERR_*; the
+ *     offending item is processed as documented per call, never read out of
+ *     bounds.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_ABI_VERSION 1
+
+#define ENGRAM_OK 0
+#define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
+#define ENGRAM_E_RANGE (-2)        /* start_pos+T > max_seq, T > max_tokens, ...   */
+#define ENGRAM_E_UNSUPPORTED (-3)  /* hc outside 1..4, head_dim, format, limits    */
+#define ENGRAM_E_STATE (-4)        /* call order of the stateful context           */
+#define ENGRAM_E_HIP (-5)          /* the HIP runtime refused a launch or copy     */
+#define ENGRAM_E_DEVICE (-6)       /* engram_check: the device error word is set   */
+
+/* bits of the device error word */
+#define ENGRAM_DEVERR_TOKEN 1      /* token id < 0 or >= vocab                     */
+#define ENGRAM_DEVERR_ROW 2        /* row id < 0 or >= the table's row count       */
+
+/* limits of the hash geometry (the hash constants travel as kernel arguments) */
+#define ENGRAM_MAX_LAYERS 4
+#define ENGRAM_MAX_NGRAM 8
+#define ENGRAM_MAX_SLOTS 128       /* n_layers * (max_ngram - 1) * n_heads         */
+
+/* Q2_K row: one 84-byte super-block per 256-wide row (atlascybernetics
+ * "engram_v41.rs", ENGRAM_ROW_BYTES and module doc stage 2). */
+#define ENGRAM_Q2K_ROW_BYTES 84
+
+const char *engram_last_error(void);
+int32_t engram_abi_version(void);
+
+/* ------------------------------------------------------------------ hash */
+
+/* The hash tables (atlascybernetics "engram_v41.rs", EngramHashTables and
+ * from_flat).  cols = (max_ngram - 1) * n_heads; slot (n-2)*n_heads + head
+ * holds the constants of n-gram size n (2..max_ngram) and head `head`.
+ *   n_layers in 1..ENGRAM_MAX_LAYERS, max_ngram in 2..ENGRAM_MAX_NGRAM,
+ *   n_heads >= 1, n_layers * cols <= ENGRAM_MAX_SLOTS;
+ *   d_token_map [vocab] int64, device: compressed id of every token, -1 =
+ *               unmapped (treated as pad and blocking every larger shift);
+ *   pad_id      the pad token's compressed id (token_map[pad token]);
+ *   multipliers [n_layers][max_ngram] host, each >= 0 (the pages' tables are
+ *               unsigned values that must fit i64);
+ *   primes      [n_layers][cols] host, each > 0;
+ *   offsets     [n_layers][cols] host, each >= 0, offset + prime <= 2^62. */
+typedef struct engram_hash_tables {
+    int32_t n_layers;
+    int32_t max_ngram;
+    int32_t n_heads;
+    int32_t reserved;
+    int64_t vocab;
+    int64_t pad_id;
+    const int64_t *d_token_map;
+    const int64_t *multipliers;
+    const int64_t *primes;
+    const int64_t *offsets;
+} engram_hash_tables;
+
+/* Hash T tokens placed at positions start_pos .. start_pos+T-1
+ * (atlascybernetics "engram_v41.rs", EngramHasher::hash; metrale
+ * "engram.rs", NgramHashState::forward).
+ *   d_ids      [T] int32 token ids;
+ *   d_history  [max_seq] int64, the sequence's compressed-id cache: read at
+ *              positions < start_pos (look-back of the previous calls;
+ *              never-written positions must hold 0, as the zero-initialised
+ *              cache does), written at start_pos .. start_pos+T-1;
+ *   d_row_ids  [T][n_layers][cols] int64 output:
+ *              id = rem_euclid(window hash, prime) + offset, the window hash
+ *              of n-gram size n being the XOR over shifts i < n of
+ *              token[i] * multiplier[i] in wrapping 64-bit arithmetic, with
+ *              the sticky pad rule of the pages;
+ *   d_err      nullable; a token id outside [0, vocab) sets
+ *              ENGRAM_DEVERR_TOKEN and is hashed as an unmapped (-1) token.
+ * Refuses (ENGRAM_E_RANGE) start_pos + T > max_seq. T = 0 is a no-op. */
+int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int64_t T,
+                    int64_t start_pos, int64_t *d_history, int64_t max_seq,
+                    int64_t *d_row_ids, int32_t *d_err, void *stream);
+
+/* -------------------------------------------------------- gather + dequant */
+
+#define ENGRAM_FMT_Q2K 0
+#define ENGRAM_FMT_E4M3 1
+
+/* One layer's table, resident in device memory.
+ *   ENGRAM_FMT_Q2K: d_data [n_rows][84] Q2_K blocks (16 bytes of 4-bit
+ *       scale/min pairs, 64 bytes of 2-bit quants, fp16 d, fp16 dmin; GGML's
+ *       k-quant block, which the pages name by size only), head_dim = 256,
+ *       d_scales = NULL;
+ *   ENGRAM_FMT_E4M3: d_data [n_rows][head_dim] fp8 e4m3fn codes, d_scales
+ *       [n_rows][head_dim/scale_block] f32 powers of two (metrale
+ *       "engram.rs", EngramTables: scales per scale_block values);
+ *       head_dim a multiple of 16 up to 1024, scale_block a multiple of 16
+ *       dividing head_dim. */
+typedef struct engram_table {
+    int32_t fmt;
+    int32_t head_dim;
+    int32_t scale_block;
+    int32_t reserved;
+    int64_t n_rows;
+    const uint8_t *d_data;
+    const float *d_scales;
+} engram_table;
+
+/* rows[t*cols + c] = dequant(table row d_row_ids[t*id_stride + c]) as bf16
+ * (atlascybernetics "engram_v41.rs", rows_from_q2k and layer_row_ids;
+ * metrale "engram.rs", regen_table and embed_rows).  Q2_K: y = d*scale*q -
+ * dmin*min rounded once to bf16; e4m3: y = bf16(e4m3 value * block scale).
+ *   d_row_ids  ids of token t at d_row_ids + t*id_stride (id_stride >= cols;
+ *              for layer l of an engram_hash output pass
+ *              d_row_ids + l*cols and id_stride = n_layers*cols);
+ *   d_rows     [T*cols][head_dim] bf16 output, i.e. [T][cols*head_dim];
+ *   d_err      nullable; an id outside [0, n_rows) sets ENGRAM_DEVERR_ROW and
+ *              its row is written as zeros. */
+int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_ids, int64_t T,
+                              int32_t cols, int64_t id_stride, uint16_t *d_rows,
+                              int32_t *d_err, void *stream);
+
+/* ------------------------------------------------------------- projection */
+
+/* y[t][n] = bf16( sum_k x[t][k] * w[n][k] ) with f32 accumulation
+ * (metrale "engram.rs", linear_bf16; atlascybernetics "engram_v41.rs",
+ * module doc stage 3: [tokens, cols*head_dim] x wkv^T -> [tokens,
+ * dim*(hc+1)]).  A bandwidth-bound GEMV serves T <= 4, the MFMA GEMM larger T.
+ *   d_x [T][K], d_w [N][K], d_y [T][N], all bf16; K a multiple of 64. */
+int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
+                       int64_t K, int64_t N, void *stream);
+
+/* ------------------------------------------------------------------- gate */
+
+/* qk[i] = f32(q[i]) * f32(k[i]) for n values (atlascybernetics
+ * "engram_v41.rs", EngramV41::upload_qk): the gate's [hc][dim] weight. */
+int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk, int64_t n,
+                          void *stream);
+
+/* In place on the FP32 highway h [T][hc][dim] (metrale "engram.rs",
+ * gate_and_add; atlascybernetics "engram_v41.rs", module doc stage 4): for
+ * each token t and stream c, with key = kv[t][c*dim ..], value =
+ * kv[t][hc*dim ..]:
+ *   s    = (sum h*qk*key) / sqrt(sum h^2/dim + eps) / sqrt(sum key^2/dim + eps)
+ *          / sqrt(dim)
+ *   gate = sigmoid(sign(s) * sqrt(max(|s|, 1e-6)))
+ *   h   += gate * value          (kept in f32)
+ *   d_kv [T][dim*(hc+1)] bf16, d_qk [hc][dim] f32; hc in 1..4 (EngramV41::new),
+ *   dim a multiple of 256. */
+int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, int64_t T,
+                          int32_t hc, int64_t dim, float eps, void *stream);
+
+/* --------------------------------------------------- stateful engram layer */
+
+/* One sequence's engram: hash tables, up to n_layers registered layers and a
+ * caller-owned workspace holding the hasher history, the step's row ids, the
+ * dequantised rows, the projection output and the device error word
+ * (atlascybernetics "engram_v41.rs", EngramV41 and EngramHasher;
+ * "deepseek_v41_layer.rs", V41Runtime::step_hashes).  One context serves one
+ * sequence; calls on one context must not overlap. */
+typedef struct engram_ctx engram_ctx;
+
+/* Geometry: hc in 1..4; dim a multiple of 256; head_dim of every layer's
+ * table; eps of the gate; max_tokens per call; max_seq positions of history.
+ * hash.multipliers/primes/offsets are copied at create. */
+typedef struct engram_config {
+    int32_t hc;
+    int32_t head_dim;
+    int64_t dim;
+    float eps;
+    int32_t reserved;
+    int64_t max_tokens;
+    int64_t max_seq;
+    engram_hash_tables hash;
+} engram_config;
+
+/* Device bytes the workspace needs for cfg (0 if cfg is invalid). */
+size_t engram_workspace_bytes(const engram_config *cfg);
+
+/* Validates cfg, carves d_workspace (>= engram_workspace_bytes(cfg) bytes,
+ * 256-byte aligned, caller-owned, must outlive the context) and returns a
+ * host-side context in *out.  Call engram_reset before the first forward. */
+int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t workspace_bytes,
+                          engram_ctx **out);
+
+/* Registers layer hash_index (0 .. n_layers-1): its table, wkv [dim*(hc+1)]
+ * [cols*head_dim] bf16 and qk [hc][dim] f32 (atlascybernetics
+ * "engram_v41.rs", add_layer and EngramLayerWeights).  Refuses a table with
+ * fewer rows than max(offset + prime) of that layer, so every hashed id is a
+ * valid row.  Re-registering replaces the layer's pointers. */
+int32_t engram_ctx_add_layer(engram_ctx *ctx, int32_t hash_index, const engram_table *table,
+                             const uint16_t *d_wkv, const float *d_qk);
+
+/* History := 0, position := 0, device error word := 0, no step open. */
+int32_t engram_reset(engram_ctx *ctx, void *stream);
+
+/* One engram layer over the next T tokens of the sequence, gating d_h
+ * [T][hc][dim] in place.  hash_index 0 opens a step: it hashes the T tokens
+ * d_ids [T] for every layer at the current position and advances the
+ * position by T (the look-back carries across prefill chunks and decode
+ * steps).  hash_index > 0 reuses the open step's row ids (d_ids is ignored
+ * and may be NULL) and must pass the same T (atlascybernetics
+ * "deepseek_v41_layer.rs", V41Runtime::step_hashes: computed by the first
+ * engram layer, reused by the second).
+ * Refuses T > max_tokens or position + T > max_seq (ENGRAM_E_RANGE),
+ * an unregistered layer or a call with no open step / another T
+ * (ENGRAM_E_STATE). */
+int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids, int64_t T,
+                       float *d_h, void *stream);
+
+/* Synchronises `stream`, reads the device error word and returns
+ * ENGRAM_E_DEVICE if it is set (the word keeps its bits until engram_reset). */
+int32_t engram_check(engram_ctx *ctx, void *stream);
+
+/* Current position (tokens hashed since the last reset); -1 for NULL. */
+int64_t engram_position(const engram_ctx *ctx);
+
+/* Device views into the workspace (any output may be NULL): the open step's
+ * row ids [T][n_layers][cols] int64, the last forward's rows [T][cols*head_dim]
+ * bf16 and kv [T][dim*(hc+1)] bf16.  Valid until the next forward. */
+int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t **d_rows,
+                           uint16_t **d_kv, int32_t **d_err);
+
+/* Stage timing with HIP events recorded on the forward's stream, around each
+ * kernel of every engram_forward while enabled (stages: 0 hash, 1 gather,
+ * 2 projection, 3 gate).  engram_ctx_timing synchronises the events and
+ * returns, per stage, the summed milliseconds and the number of launches
+ * since timing was enabled; it then clears them. */
+int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable);
+int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage /*[4]*/,
+                          int64_t *launches_per_stage /*[4]*/);
+
+void engram_ctx_destroy(engram_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

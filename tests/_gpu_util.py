@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU parity tests: device upload of the synthetic
+workloads, the tolerance metric, and bf16 helpers.  Inputs come from
+``synth``; expected values from ``oracle``; nothing here computes a stage."""
+import functools
+import sys
+
+import numpy as np
+
+import synth
+from synth import generate as G
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def relerr(got, want):
+    """max_i |g_i - o_i| / max(|o_i|, rms(o)): elementwise relative error with
+    values below the rms measured against the rms (so cancellation in a
+    single output does not blow the ratio up)."""
+    g = np.asarray(got, dtype=np.float64).ravel()
+    o = np.asarray(want, dtype=np.float64).ravel()
+    rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
+    den = np.maximum(np.abs(o), rms)
+    den[den == 0] = 1.0
+    return float(np.max(np.abs(g - o) / den)) if o.size else 0.0
+
+
+def widen(bits):
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def to_np_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=4)
+def family_data(name):
+    """Host arrays of a workload: hash tables and every layer's inputs."""
+    w = synth.WORKLOADS[name]
+    ht = G.hash_tables(w)
+    layers = [G.layer_inputs(w, ht, l) for l in range(w.n_layers)]
+    return w, ht, layers
+
+
+class Device:
+    """The workload on the GPU: tables, wkv, qk, token map, hash tables."""
+
+    def __init__(self, name):
+        import torch
+        import gram_hashed_embedding_engram_amd as E
+        self.w, self.ht, self.layers = family_data(name)
+        w = self.w
+        dev = "cuda"
+        self.token_map = torch.from_numpy(self.ht["token_map"]).to(dev)
+        self.tables = E.HashTables(self.token_map, self.ht["pad_id"], self.ht["multipliers"],
+                                   self.ht["primes"], self.ht["offsets"])
+        self.tab, self.wkv, self.qk = [], [], []
+        for L in self.layers:
+            data = torch.from_numpy(L["table"]).to(dev)
+            scales = None if L["scales"] is None else torch.from_numpy(L["scales"]).to(dev)
+            self.tab.append(E.Table(data, scales, head_dim=w.head_dim, scale_block=w.scale_block))
+            self.wkv.append(torch.from_numpy(L["wkv"].view(np.int16)).to(dev))
+            q = torch.from_numpy(L["q"].view(np.int16)).to(dev)
+            k = torch.from_numpy(L["k"].view(np.int16)).to(dev)
+            qk = torch.empty(w.hc, w.dim, dtype=torch.float32, device=dev)
+            E.qk_product(q, k, qk)
+            self.qk.append(qk)
+        torch.cuda.synchronize()
+
+    def context(self, max_tokens, max_seq):
+        import gram_hashed_embedding_engram_amd as E
+        w = self.w
+        ctx = E.Context(self.tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
+        for l in range(w.n_layers):
+            ctx.add_layer(l, self.tab[l], self.wkv[l], self.qk[l])
+        ctx.reset()
+        return ctx
+
+    def oracle_hasher(self, max_seq):
+        import oracle
+        ht = self.ht
+        return oracle.Hasher(ht["token_map"], ht["pad_id"], ht["multipliers"], ht["primes"],
+                             ht["offsets"], max_seq)
+
+    def oracle_rows(self, layer, ids):
+        import oracle
+        L = self.layers[layer]
+        return oracle.gather(L["table"], L["scales"], ids, self.w.head_dim, self.w.scale_block)

@@ -1,0 +1,226 @@
+"""The C ABI on the host, without a GPU: libengram.so loads, exports every
+function include/engram.h declares, and refuses bad arguments before any
+launch (metrale "engram_v41" module index, invariants: refusals happen before
+any copy or launch).  Every call here is refused by the host checks, so no
+kernel is launched; fake device addresses are never dereferenced."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gram_hashed_embedding_engram_amd as E
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "engram.h")
+FAKE = 0x7F0000000000          # 256-byte aligned stand-in for device memory
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(E.LIB_PATH):
+        import gram_hashed_embedding_engram_amd.build as B
+        B.build()
+    return E.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(E.EXPORTS) == names
+    assert L.engram_abi_version() == 1
+
+
+def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
+    cols = (ng - 1) * nh
+    mult = np.ones((nl, ng), np.int64) * 3 if mult is None else mult
+    primes = np.full((nl, cols), 101, np.int64) if primes is None else primes
+    offsets = (np.arange(nl * cols, dtype=np.int64).reshape(nl, cols) * 101
+               if offsets is None else offsets)
+    keep = (mult, primes, offsets)
+    c = E.HashTablesC(nl, ng, nh, 0, vocab, 0, FAKE, mult.ctypes.data, primes.ctypes.data,
+                      offsets.ctypes.data)
+    return c, keep
+
+
+def rc_msg(rc):
+    return rc, E.last_error()
+
+
+def test_hash_refusals(L):
+    c, keep = tables_c()
+    call = lambda tab, T=4, start=0, max_seq=16: rc_msg(L.engram_hash(
+        ctypes.byref(tab), FAKE, T, start, FAKE, max_seq, FAKE, None, None))
+    rc, msg = call(c, T=10, start=8, max_seq=16)
+    assert rc == E.E_RANGE and "16 positions, 18 needed" in msg
+    bad, k2 = tables_c(ng=1)
+    assert call(bad)[0] == E.E_ARG
+    bad, k3 = tables_c(ng=9, primes=np.full((2, 64), 101, np.int64),
+                       offsets=np.zeros((2, 64), np.int64), mult=np.ones((2, 9), np.int64))
+    assert call(bad)[0] == E.E_UNSUPPORTED
+    bad, k4 = tables_c(nl=5, mult=np.ones((5, 4), np.int64),
+                       primes=np.full((5, 24), 7, np.int64), offsets=np.zeros((5, 24), np.int64))
+    assert call(bad)[0] == E.E_UNSUPPORTED
+    m = np.ones((2, 4), np.int64)
+    m[1, 2] = -5
+    bad, k5 = tables_c(mult=m)
+    rc, msg = call(bad)
+    assert rc == E.E_ARG and "multipliers" in msg
+    p = np.full((2, 24), 101, np.int64)
+    p[0, 3] = 0
+    bad, k6 = tables_c(primes=p)
+    rc, msg = call(bad)
+    assert rc == E.E_ARG and "primes" in msg
+    o = np.zeros((2, 24), np.int64)
+    o[1, 1] = -1
+    bad, k7 = tables_c(offsets=o)
+    assert call(bad)[0] == E.E_ARG
+    # NULL pointers
+    assert L.engram_hash(ctypes.byref(c), None, 4, 0, FAKE, 16, FAKE, None, None) == E.E_ARG
+    assert L.engram_hash(None, FAKE, 4, 0, FAKE, 16, FAKE, None, None) == E.E_ARG
+
+
+def test_gather_refusals(L):
+    t = E.TableC(E.FMT_Q2K, 128, 0, 0, 100, FAKE, None)
+    rc, msg = rc_msg(L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None, None))
+    assert rc == E.E_UNSUPPORTED and "head_dim must be 256" in msg
+    t = E.TableC(E.FMT_Q2K, 256, 0, 0, 100, FAKE + 2, None)
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None, None) == E.E_ARG
+    t = E.TableC(E.FMT_E4M3, 256, 100, 0, 100, FAKE, FAKE)
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None,
+                                   None) == E.E_UNSUPPORTED
+    t = E.TableC(E.FMT_E4M3, 256, 128, 0, 100, FAKE, None)
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None, None) == E.E_ARG
+    t = E.TableC(7, 256, 128, 0, 100, FAKE, FAKE)
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None,
+                                   None) == E.E_UNSUPPORTED
+    t = E.TableC(E.FMT_Q2K, 256, 0, 0, 100, FAKE, None)
+    # id_stride below cols, misaligned output
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 23, FAKE, None, None) == E.E_ARG
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE + 8, None,
+                                   None) == E.E_ARG
+    # T = 0 is a no-op that launches nothing
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 0, 24, 48, FAKE, None, None) == E.OK
+
+
+def test_project_refusals(L):
+    assert L.engram_project(FAKE, FAKE, FAKE, 4, 100, 256, None) == E.E_UNSUPPORTED
+    assert L.engram_project(FAKE, FAKE, FAKE, 4, 6144, 20481, None) == E.E_UNSUPPORTED
+    assert L.engram_project(FAKE, FAKE, FAKE, -1, 6144, 20480, None) == E.E_ARG
+    assert L.engram_project(None, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
+    assert L.engram_project(FAKE + 8, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
+    assert L.engram_project(FAKE, FAKE, FAKE, 1 << 20, 1 << 14, 64, None) == E.E_UNSUPPORTED
+    assert L.engram_project(FAKE, FAKE, FAKE, 0, 6144, 20480, None) == E.OK
+
+
+def test_gate_refusals(L):
+    f = lambda T=4, hc=4, dim=4096, eps=1e-6, h=FAKE: L.engram_gate_apply(
+        h, FAKE, FAKE, T, hc, dim, ctypes.c_float(eps), None)
+    assert f(hc=0) == E.E_UNSUPPORTED and f(hc=5) == E.E_UNSUPPORTED
+    assert f(dim=300) == E.E_UNSUPPORTED
+    assert f(eps=float("nan")) == E.E_ARG and f(eps=-1.0) == E.E_ARG
+    assert f(h=None) == E.E_ARG and f(h=FAKE + 4) == E.E_ARG
+    assert L.engram_qk_product(None, FAKE, FAKE, 10, None) == E.E_ARG
+    assert L.engram_qk_product(FAKE, FAKE, FAKE, 0, None) == E.OK
+
+
+def make_cfg(max_tokens=64, max_seq=512, hc=4, dim=4096, head_dim=256, tables=None):
+    c, keep = tables or tables_c()
+    cfg = E.ConfigC(hc, head_dim, dim, 1e-6, 0, max_tokens, max_seq, c)
+    return cfg, keep
+
+
+def test_workspace_layout(L):
+    cfg, keep = make_cfg()
+    n = L.engram_workspace_bytes(ctypes.byref(cfg))
+    r256 = lambda v: (v + 255) // 256 * 256
+    want = (r256(8 * 512) + r256(8 * 64 * 2 * 24) + r256(2 * 64 * 24 * 256)
+            + r256(2 * 64 * 4096 * 5) + 256)
+    assert n == want
+    bad, _ = make_cfg(max_tokens=0)
+    assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_context_refusals_and_state(L):
+    cfg, keep = make_cfg()
+    n = L.engram_workspace_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    assert L.engram_ctx_create(ctypes.byref(cfg), FAKE, n - 1, ctypes.byref(h)) == E.E_RANGE
+    assert L.engram_ctx_create(ctypes.byref(cfg), FAKE + 16, n, ctypes.byref(h)) == E.E_ARG
+    bad, k2 = make_cfg(hc=5)
+    assert L.engram_ctx_create(ctypes.byref(bad), FAKE, 1 << 40, ctypes.byref(h)) \
+        == E.E_UNSUPPORTED
+    bad, k3 = make_cfg(dim=1000)
+    assert L.engram_ctx_create(ctypes.byref(bad), FAKE, 1 << 40, ctypes.byref(h)) \
+        == E.E_UNSUPPORTED
+    assert L.engram_ctx_create(ctypes.byref(cfg), FAKE, n, ctypes.byref(h)) == E.OK
+    try:
+        assert L.engram_position(h) == 0
+        ptrs = [ctypes.c_void_p() for _ in range(4)]
+        assert L.engram_ctx_buffers(h, *[ctypes.byref(p) for p in ptrs]) == E.OK
+        hist, rid, rows, kv, err = FAKE, *[p.value for p in ptrs]
+        assert rid == FAKE + 4096 and rows == rid + 8 * 64 * 48
+        assert err == FAKE + n - 256
+        # forward before any layer is registered
+        rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 1, FAKE, None))
+        assert rc == E.E_STATE and "no weights" in msg
+        # the table must cover every hashed id of the layer: max(offset+prime) =
+        # 47*101 + 101 = 4848 rows for layer 1
+        tab = E.TableC(E.FMT_Q2K, 256, 0, 0, 4847, FAKE, None)
+        rc, msg = rc_msg(L.engram_ctx_add_layer(h, 1, ctypes.byref(tab), FAKE, FAKE))
+        assert rc == E.E_RANGE and "reaches row 4847" in msg
+        tab = E.TableC(E.FMT_Q2K, 256, 0, 0, 4848, FAKE, None)
+        assert L.engram_ctx_add_layer(h, 1, ctypes.byref(tab), FAKE, FAKE) == E.OK
+        assert L.engram_ctx_add_layer(h, 2, ctypes.byref(tab), FAKE, FAKE) == E.E_ARG
+        tab128 = E.TableC(E.FMT_E4M3, 128, 128, 0, 5000, FAKE, FAKE)
+        assert L.engram_ctx_add_layer(h, 0, ctypes.byref(tab128), FAKE, FAKE) == E.E_ARG
+        tab0 = E.TableC(E.FMT_Q2K, 256, 0, 0, 2424, FAKE, None)
+        assert L.engram_ctx_add_layer(h, 0, ctypes.byref(tab0), FAKE, FAKE) == E.OK
+        # layer 1 before layer 0 opened a step
+        rc, msg = rc_msg(L.engram_forward(h, 1, None, 1, FAKE, None))
+        assert rc == E.E_STATE and "before layer 0" in msg
+        # too many tokens, too many positions, bad arguments
+        assert L.engram_forward(h, 0, FAKE, 65, FAKE, None) == E.E_RANGE
+        assert L.engram_forward(h, 0, FAKE, 0, FAKE, None) == E.E_ARG
+        assert L.engram_forward(h, 0, None, 1, FAKE, None) == E.E_ARG
+        assert L.engram_forward(h, 0, FAKE, 1, FAKE + 4, None) == E.E_ARG
+        assert L.engram_forward(h, 3, FAKE, 1, FAKE, None) == E.E_ARG
+        # timing with nothing recorded makes no runtime call
+        assert L.engram_ctx_set_timing(h, 1) == E.OK
+        ms = (ctypes.c_double * 4)()
+        cnt = (ctypes.c_int64 * 4)()
+        assert L.engram_ctx_timing(h, ms, cnt) == E.OK and list(cnt) == [0, 0, 0, 0]
+    finally:
+        L.engram_ctx_destroy(h)
+    L.engram_ctx_destroy(None)
+    assert L.engram_position(None) == -1
+
+
+def test_position_limit(L):
+    cfg, keep = make_cfg(max_tokens=64, max_seq=16)
+    n = L.engram_workspace_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    assert L.engram_ctx_create(ctypes.byref(cfg), FAKE, n, ctypes.byref(h)) == E.OK
+    try:
+        tab = E.TableC(E.FMT_Q2K, 256, 0, 0, 1 << 20, FAKE, None)
+        assert L.engram_ctx_add_layer(h, 0, ctypes.byref(tab), FAKE, FAKE) == E.OK
+        rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 17, FAKE, None))
+        assert rc == E.E_RANGE and "16 positions, 17 needed" in msg
+    finally:
+        L.engram_ctx_destroy(h)
+
+
+def test_binding_without_library(monkeypatch, tmp_path):
+    """The binding has no fallback: a missing library raises."""
+    monkeypatch.setattr(E, "_lib", None)
+    monkeypatch.setattr(E, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        E.lib()

@@ -1,0 +1,219 @@
+"""GPU parity of the fused, stateful engram_forward on the five synthetic
+workloads (run on an MI355X).
+
+The chain is checked stage by stage on the GPU's own intermediates: hash ids
+(bit for bit against the oracle hasher fed the same token stream), rows (bit
+for bit against the oracle gather of the oracle ids), kv (relative error
+<= 1e-2 against the oracle projection of the rows), highway (relative error
+<= 2e-3 against the oracle gate applied to the GPU's kv).  Large workloads
+are checked on all hash ids and rows and on sampled tokens / output columns
+for kv.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import generate as G
+from _gpu_util import Device, log, relerr, widen, to_np_u16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def E():
+    import gram_hashed_embedding_engram_amd as E
+    E.lib()
+    return E
+
+
+def cuda(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_call(dev, ctx, layer, ids_np, hasher_out, h_before, h_after, T, sample_tokens=None,
+               sample_cols=None, label=""):
+    """Compare one forward call's intermediates and output with the oracle."""
+    w = dev.w
+    rid, rows, kv = ctx.views(T)
+    rid = rid.cpu().numpy()
+    np.testing.assert_array_equal(rid, hasher_out, err_msg=f"{label} hash ids")
+    rows = to_np_u16(rows)
+    want_rows = dev.oracle_rows(layer, hasher_out[:, layer, :]).reshape(T, -1)
+    np.testing.assert_array_equal(rows, want_rows, err_msg=f"{label} rows")
+    kv = to_np_u16(kv)
+    toks = np.arange(T) if sample_tokens is None else sample_tokens
+    want_kv = oracle.linear_bf16(rows[toks], dev.layers[layer]["wkv"])
+    e_kv = relerr(widen(kv[toks]), widen(want_kv))
+    assert e_kv <= 1e-2, f"{label} kv relerr {e_kv:.2e}"
+    if sample_cols is not None:
+        want_c = oracle.linear_bf16(rows, dev.layers[layer]["wkv"][sample_cols])
+        e_c = relerr(widen(kv[:, sample_cols]), widen(want_c))
+        assert e_c <= 1e-2, f"{label} kv cols relerr {e_c:.2e}"
+    L = dev.layers[layer]
+    want_h = oracle.gate_and_add(h_before[toks], kv[toks], L["q"], L["k"], w.eps)
+    e_h = relerr(h_after[toks], want_h)
+    assert e_h <= 2e-3, f"{label} highway relerr {e_h:.2e}"
+    return e_kv, e_h, kv
+
+
+def test_forward_tiny(E):
+    w = synth.TINY_E4M3
+    log("forward: tiny e4m3 T=64")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    h0 = G.highway(w, w.prompt)
+    ctx = dev.context(max_tokens=64, max_seq=64)
+    d_h = torch.from_numpy(h0).cuda()
+    ctx.forward(0, cuda(ids.astype(np.int32)), 64, d_h)
+    ctx.check()
+    assert ctx.position == 64
+    h1 = d_h.cpu().numpy()
+    want_ids = dev.oracle_hasher(64).hash(ids, 0)
+    e_kv, e_h, kv = check_call(dev, ctx, 0, ids, want_ids, h0, h1, 64, label="tiny")
+    # the fully oracle chain (diagnostic: differs from the GPU's by kv rounding)
+    rows = dev.oracle_rows(0, want_ids[:, 0, :]).reshape(64, -1)
+    kv_o = oracle.linear_bf16(rows, dev.layers[0]["wkv"])
+    h_o = oracle.gate_and_add(h0, kv_o, dev.layers[0]["q"], dev.layers[0]["k"], w.eps)
+    log(f"  kv {e_kv:.2e}  highway {e_h:.2e}  full-oracle highway {relerr(h1, h_o):.2e}"
+        f"  kv bits differing {(kv != kv_o).mean():.2e}")
+    # the rows themselves: e4m3 times a power of two is exact in bf16
+    assert relerr(h1, h_o) < 2e-2
+
+
+def test_forward_decode_workload(E):
+    """32-token prompt, then 256 single-token steps over both layers."""
+    w = synth.DECODE_Q2K
+    log("forward: decode Q2_K, prompt 32 + 256 steps, 2 layers")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    max_seq = w.total_tokens
+    ctx = dev.context(max_tokens=32, max_seq=max_seq)
+    hasher = dev.oracle_hasher(max_seq)
+    d_ids = cuda(ids.astype(np.int32))
+    prompt_h = G.highway(w, w.prompt)
+    step_h = G.highway(w, w.decode_steps, decode=True)
+    worst = [0.0, 0.0]
+    pos = 0
+    for step in range(1 + w.decode_steps):
+        T = w.prompt if step == 0 else 1
+        h0 = prompt_h if step == 0 else step_h[step - 1:step]
+        want_ids = hasher.hash(ids[pos:pos + T], pos)
+        for layer in range(2):
+            d_h = torch.from_numpy(h0).cuda()
+            ctx.forward(layer, d_ids[pos:pos + T] if layer == 0 else None, T, d_h)
+            h1 = d_h.cpu().numpy()
+            e_kv, e_h, _ = check_call(dev, ctx, layer, ids[pos:pos + T], want_ids, h0, h1, T,
+                                      label=f"step {step} layer {layer}")
+            worst = [max(worst[0], e_kv), max(worst[1], e_h)]
+        pos += T
+        assert ctx.position == pos
+    ctx.check()
+    log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
+
+
+def test_forward_prefill_workload(E):
+    """T = 4096 Zipf tokens through both layers with one hash pass."""
+    w = synth.PREFILL_Q2K
+    log("forward: prefill Q2_K T=4096, 2 layers")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    T = w.prompt
+    h0 = G.highway(w, T)
+    ctx = dev.context(max_tokens=T, max_seq=T)
+    want_ids = dev.oracle_hasher(T).hash(ids, 0)
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.integers(0, T, 11)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, 20479], rng.integers(0, 20480, 12)]))
+    d_ids = cuda(ids.astype(np.int32))
+    for layer in range(2):
+        d_h = torch.from_numpy(h0).cuda()
+        ctx.forward(layer, d_ids if layer == 0 else None, T, d_h)
+        h1 = d_h.cpu().numpy()
+        e_kv, e_h, _ = check_call(dev, ctx, layer, ids, want_ids, h0, h1, T, toks, cols,
+                                  label=f"prefill layer {layer}")
+        log(f"  layer {layer}: kv {e_kv:.2e} highway {e_h:.2e}")
+    ctx.check()
+
+
+def test_forward_split_workload(E):
+    """e4m3 tables: 8192 Zipf tokens in chunks of 2048, then 128 decode steps.
+    Each call's hash ids equal the single-pass hash of the whole sequence."""
+    w = synth.SPLIT_E4M3
+    log("forward: split e4m3, 4x2048 + 128x1, 2 layers")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    n = ids.size
+    single = dev.oracle_hasher(n).hash(ids, 0)
+    ctx = dev.context(max_tokens=w.chunk, max_seq=n)
+    d_ids = cuda(ids.astype(np.int32))
+    prompt_h = G.highway(w, w.prompt)
+    step_h = G.highway(w, w.decode_steps, decode=True)
+    bounds = list(range(0, w.prompt + 1, w.chunk)) + list(range(w.prompt + 1, n + 1))
+    rng = np.random.default_rng(3)
+    for ci, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        T = b - a
+        h0 = prompt_h[a:b] if a < w.prompt else step_h[a - w.prompt:b - w.prompt]
+        full_check = T > 1 or ci % 16 == 0
+        for layer in range(2):
+            d_h = torch.from_numpy(h0).cuda()
+            ctx.forward(layer, d_ids[a:b] if layer == 0 else None, T, d_h)
+            if full_check:
+                toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 6)]))
+                check_call(dev, ctx, layer, ids[a:b], single[a:b], h0, d_h.cpu().numpy(), T,
+                           toks, label=f"split call {ci} layer {layer}")
+            else:
+                rid = ctx.views(T)[0].cpu().numpy()
+                np.testing.assert_array_equal(rid, single[a:b])
+    assert ctx.position == n
+    ctx.check()
+
+
+def test_forward_gather_stress(E):
+    """One Q2_K layer over ~75M rows (6.3 GB), T = 16384 uniform tokens."""
+    w = synth.GATHER_Q2K
+    log("forward: gather stress Q2_K, 75M-row table, T=16384")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    T = w.prompt
+    h0 = G.highway(w, T)
+    ctx = dev.context(max_tokens=T, max_seq=T)
+    d_h = torch.from_numpy(h0).cuda()
+    ctx.forward(0, cuda(ids.astype(np.int32)), T, d_h)
+    ctx.check()
+    want_ids = dev.oracle_hasher(T).hash(ids, 0)
+    rng = np.random.default_rng(4)
+    toks = np.unique(np.concatenate([[0, T - 1, 8191, 8192], rng.integers(0, T, 8)]))
+    cols = np.unique(np.concatenate([[0, 20479], rng.integers(0, 20480, 6)]))
+    e_kv, e_h, _ = check_call(dev, ctx, 0, ids, want_ids, h0, d_h.cpu().numpy(), T, toks, cols,
+                              label="gather stress")
+    log(f"  kv {e_kv:.2e} highway {e_h:.2e}")
+
+
+def test_forward_deterministic_and_device_error(E):
+    w = synth.TINY_E4M3
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    h0 = G.highway(w, 64)
+    outs = []
+    for _ in range(2):
+        ctx = dev.context(max_tokens=64, max_seq=128)
+        d_h = torch.from_numpy(h0).cuda()
+        ctx.forward(0, cuda(ids.astype(np.int32)), 64, d_h)
+        outs.append(d_h.cpu().numpy().view(np.uint32))
+        ctx.check()
+    np.testing.assert_array_equal(outs[0], outs[1])
+    bad = ids.copy()
+    bad[5] = w.vocab + 3
+    ctx = dev.context(max_tokens=64, max_seq=128)
+    d_h = torch.from_numpy(h0).cuda()
+    ctx.forward(0, cuda(bad.astype(np.int32)), 64, d_h)
+    with pytest.raises(E.EngramError) as ei:
+        ctx.check()
+    assert ei.value.code == E.E_DEVICE
+    ctx.reset()
+    ctx.check()

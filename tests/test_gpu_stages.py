@@ -1,0 +1,294 @@
+"""GPU parity of each C-ABI entry point against the oracle, on seeded
+synthetic inputs (run on an MI355X).
+
+Bars: hash ids and dequantised rows bit for bit; the projection within a
+relative error of 1e-2 and the gated highway within 2e-3 (metric: _gpu_util
+.relerr).  Shapes cover several tiles with ragged tails, the full workload
+shapes (K = 6144, N = 20480, dim = 4096), and the degenerate cases (T = 0,
+bad ids, unmapped windows).
+"""
+import numpy as np
+import pytest
+
+import synth
+from synth import generate as G
+from _gpu_util import Device, log, relerr, widen, to_np_u16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def E():
+    import gram_hashed_embedding_engram_amd as E
+    E.lib()
+    return E
+
+
+@pytest.fixture(scope="module")
+def tiny(E):
+    log("setup: tiny e4m3 workload")
+    return Device(synth.TINY_E4M3.name)
+
+
+@pytest.fixture(scope="module")
+def decode(E):
+    log("setup: decode Q2_K workload (2 layers, 4.6M rows, wkv 20480x6144)")
+    return Device(synth.DECODE_Q2K.name)
+
+
+def bf16_rand(rng, shape, std):
+    x = (rng.standard_normal(shape) * std).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def cuda(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ------------------------------------------------------------------ hash
+def run_hash(E, dev, ids, start, hist):
+    T = ids.size
+    out = torch.empty(T, dev.w.n_layers, dev.w.cols, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    E.hash(dev.tables, cuda(ids.astype(np.int32)), start, hist, out, err)
+    return out.cpu().numpy(), int(err.item())
+
+
+def test_hash_tiny(E, tiny):
+    log("hash: tiny T=64 single pass")
+    ids = G.token_ids(tiny.w)
+    hist = torch.zeros(256, dtype=torch.int64, device="cuda")
+    got, err = run_hash(E, tiny, ids, 0, hist)
+    want = tiny.oracle_hasher(256).hash(ids, 0)
+    assert err == 0
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(hist[:64].cpu().numpy(), tiny.ht["token_map"][ids])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hash_chunked_equals_single_pass(E, tiny, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, tiny.w.vocab, size=300)
+    cuts = np.unique(np.concatenate([[0, 300], rng.integers(0, 300, size=12)]))
+    log(f"hash: tiny chunked at {cuts.tolist()}")
+    hist = torch.zeros(300, dtype=torch.int64, device="cuda")
+    parts = [run_hash(E, tiny, ids[a:b], a, hist)[0] for a, b in zip(cuts[:-1], cuts[1:])]
+    want = tiny.oracle_hasher(300).hash(ids, 0)
+    np.testing.assert_array_equal(np.concatenate(parts), want)
+
+
+def test_hash_split_workload(E):
+    """8192 Zipf tokens in 4 chunks of 2048, then 128 single-token steps: every
+    call equals the single-pass hash of the 8320-token sequence."""
+    import oracle
+    w = synth.SPLIT_E4M3
+    ht = G.hash_tables(w)
+    tm = torch.from_numpy(ht["token_map"]).cuda()
+    tables = E.HashTables(tm, ht["pad_id"], ht["multipliers"], ht["primes"], ht["offsets"])
+    ids = G.token_ids(w)
+    n = ids.size
+    log(f"hash: split workload {n} tokens, 4x2048 + 128x1")
+    hist = torch.zeros(n, dtype=torch.int64, device="cuda")
+    d_ids = cuda(ids.astype(np.int32))
+    out = torch.empty(n, w.n_layers, w.cols, dtype=torch.int64, device="cuda")
+    bounds = [0, 2048, 4096, 6144, 8192] + list(range(8193, n + 1))
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        E.hash(tables, d_ids[a:b], a, hist, out[a:b])
+    chunked = out.cpu().numpy()
+    hist2 = torch.zeros(n, dtype=torch.int64, device="cuda")
+    out2 = torch.empty_like(out)
+    E.hash(tables, d_ids, 0, hist2, out2)
+    want = oracle.Hasher(ht["token_map"], ht["pad_id"], ht["multipliers"], ht["primes"],
+                         ht["offsets"], n).hash(ids, 0)
+    np.testing.assert_array_equal(out2.cpu().numpy(), want)
+    np.testing.assert_array_equal(chunked, want)
+    lo = ht["offsets"][None]
+    assert (want >= lo).all() and (want < lo + ht["primes"][None]).all()
+
+
+def test_hash_bad_token_ids(E, tiny):
+    """An id outside the vocabulary raises the error bit and is hashed as an
+    unmapped token; the oracle refuses it, so it is compared on the same
+    stream with that id replaced by a vocabulary id that maps to -1."""
+    ids = G.token_ids(tiny.w)[:40].copy()
+    unmapped = int(np.nonzero(tiny.ht["token_map"] == -1)[0][0])
+    bad = ids.copy()
+    bad[[3, 17]] = [tiny.w.vocab, -5]
+    subst = ids.copy()
+    subst[[3, 17]] = unmapped
+    hist = torch.zeros(64, dtype=torch.int64, device="cuda")
+    got, err = run_hash(E, tiny, bad, 0, hist)
+    assert err == E.DEVERR_TOKEN
+    np.testing.assert_array_equal(got, tiny.oracle_hasher(64).hash(subst, 0))
+
+
+def test_hash_start_pos_and_empty(E, tiny):
+    ids = G.token_ids(tiny.w)[:10]
+    hist = torch.zeros(64, dtype=torch.int64, device="cuda")
+    got, _ = run_hash(E, tiny, ids, 20, hist)
+    np.testing.assert_array_equal(got, tiny.oracle_hasher(64).hash(ids, 20))
+    out = torch.empty(0, 1, 4, dtype=torch.int64, device="cuda")
+    E.hash(tiny.tables, torch.empty(0, dtype=torch.int32, device="cuda"), 0, hist, out)
+
+
+# --------------------------------------------------------------- gather
+def run_gather(E, dev, layer, ids2d, id_stride=None):
+    T, cols = ids2d.shape
+    id_stride = id_stride or cols
+    full = np.zeros((T, id_stride), dtype=np.int64)
+    full[:, :cols] = ids2d
+    rows = torch.empty(T * cols, dev.w.head_dim, dtype=torch.int16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    E.gather_dequant(dev.tab[layer], cuda(full), T, cols, id_stride, rows, err)
+    return to_np_u16(rows), int(err.item())
+
+
+@pytest.mark.parametrize("T", [1, 5, 37, 300])
+def test_gather_q2k(E, decode, T):
+    rng = np.random.default_rng(T)
+    for layer in range(2):
+        n = decode.layers[layer]["rows"]
+        ids = rng.integers(0, n, size=(T, 24))
+        ids[0, :3] = [0, n - 1, n // 2]
+        log(f"gather q2k: layer {layer} T={T}")
+        got, err = run_gather(E, decode, layer, ids, id_stride=48)
+        assert err == 0
+        np.testing.assert_array_equal(got, decode.oracle_rows(layer, ids))
+
+
+@pytest.mark.parametrize("T", [1, 7, 64])
+def test_gather_e4m3(E, tiny, T):
+    rng = np.random.default_rng(100 + T)
+    n = tiny.layers[0]["rows"]
+    ids = rng.integers(0, n, size=(T, 4))
+    log(f"gather e4m3: T={T}")
+    got, err = run_gather(E, tiny, 0, ids)
+    assert err == 0
+    np.testing.assert_array_equal(got, tiny.oracle_rows(0, ids))
+
+
+def test_gather_every_tiny_row(E, tiny):
+    n = tiny.layers[0]["rows"]
+    ids = np.arange(n + (-n) % 4).reshape(-1, 4) % n
+    got, _ = run_gather(E, tiny, 0, ids)
+    np.testing.assert_array_equal(got, tiny.oracle_rows(0, ids))
+
+
+def test_gather_bad_row_ids(E, tiny, decode):
+    for dev in (tiny, decode):
+        n = dev.layers[0]["rows"]
+        cols = dev.w.cols
+        ids = np.tile(np.arange(cols, dtype=np.int64), (3, 1))
+        ids[1, 2] = n
+        ids[2, 0] = -1
+        got, err = run_gather(E, dev, 0, ids)
+        assert err == E.DEVERR_ROW
+        got = got.reshape(3, cols, -1)
+        assert (got[1, 2] == 0).all() and (got[2, 0] == 0).all()
+        ok = ids.copy()
+        ok[1, 2] = ok[2, 0] = 0
+        want = dev.oracle_rows(0, ok).reshape(3, cols, -1)
+        mask = np.ones((3, cols), bool)
+        mask[1, 2] = mask[2, 0] = False
+        np.testing.assert_array_equal(got[mask], want[mask])
+
+
+# ----------------------------------------------------------- projection
+def check_project(E, x, w_dev, w_host, sample_rows=None, sample_cols=None):
+    import oracle
+    T, K = x.shape
+    N = w_host.shape[0]
+    y = torch.empty(T, N, dtype=torch.int16, device="cuda")
+    E.project(cuda(x), w_dev, y)
+    got = to_np_u16(y)
+    rows = np.arange(T) if sample_rows is None else sample_rows
+    want = oracle.linear_bf16(x[rows], w_host)
+    e = relerr(widen(got[rows]), widen(want))
+    ulp = (got[rows] != want).mean()
+    msg = f"rows: relerr {e:.2e}, {ulp:.2e} of outputs differ"
+    if sample_cols is not None:
+        want_c = oracle.linear_bf16(x, w_host[sample_cols])
+        ec = relerr(widen(got[:, sample_cols]), widen(want_c))
+        msg += f"; cols: relerr {ec:.2e}"
+        assert ec <= 1e-2, msg
+    log("  " + msg)
+    assert e <= 1e-2, msg
+    return got
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_project_gemv_decode_shape(E, decode, T):
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, decode.layers[0]["rows"], size=(T, 24))
+    x = decode.oracle_rows(0, ids).reshape(T, -1)
+    log(f"project gemv: T={T} K=6144 N=20480")
+    check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
+
+
+@pytest.mark.parametrize("M", [5, 64, 255, 257, 300, 513])
+def test_project_gemm_tiny_shape(E, tiny, M):
+    rng = np.random.default_rng(M)
+    x = bf16_rand(rng, (M, tiny.w.K), 0.5)
+    log(f"project gemm: M={M} K=1024 N=1280")
+    check_project(E, x, tiny.wkv[0], tiny.layers[0]["wkv"])
+
+
+@pytest.mark.parametrize("M", [32, 4096])
+def test_project_gemm_full_shape(E, decode, M):
+    rng = np.random.default_rng(7 + M)
+    ids = rng.integers(0, decode.layers[1]["rows"], size=(M, 24))
+    x = decode.oracle_rows(1, ids).reshape(M, -1)
+    rows = np.unique(np.concatenate([[0, M - 1, 255, 256, M // 2], rng.integers(0, M, 8)]))
+    rows = rows[rows < M]
+    cols = np.unique(np.concatenate([[0, 20479, 255, 256, 4095, 4096], rng.integers(0, 20480, 26)]))
+    log(f"project gemm: M={M} K=6144 N=20480 (sampled rows {rows.size}, cols {cols.size})")
+    check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
+
+
+def test_project_empty(E, tiny):
+    x = torch.empty(0, tiny.w.K, dtype=torch.int16, device="cuda")
+    y = torch.empty(0, tiny.w.N, dtype=torch.int16, device="cuda")
+    E.project(x, tiny.wkv[0], y)
+
+
+# ----------------------------------------------------------------- gate
+def test_qk_product_exact(E, decode):
+    L = decode.layers[0]
+    want = widen(L["q"]) * widen(L["k"])
+    np.testing.assert_array_equal(decode.qk[0].cpu().numpy().view(np.uint32),
+                                  want.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,hc,dim", [(64, 4, 256), (1, 4, 4096), (37, 3, 4096), (5, 2, 768),
+                                      (3, 1, 4352), (9, 4, 1024), (4096, 4, 4096)])
+def test_gate(E, T, hc, dim):
+    import oracle
+    rng = np.random.default_rng(T * 7 + dim)
+    h = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = bf16_rand(rng, (T, dim * (hc + 1)), 0.5)
+    q = bf16_rand(rng, (hc, dim), 0.05)
+    k = bf16_rand(rng, (hc, dim), 0.05)
+    q = (widen(q) + 1).astype(np.float32)
+    k = (widen(k) + 1).astype(np.float32)
+    qb = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    kb = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    d_qk = torch.empty(hc, dim, dtype=torch.float32, device="cuda")
+    E.qk_product(cuda(qb), cuda(kb), d_qk)
+    d_h = torch.from_numpy(h).cuda()
+    log(f"gate: T={T} hc={hc} dim={dim}")
+    E.gate_apply(d_h, cuda(kv), d_qk, 1e-6)
+    got = d_h.cpu().numpy()
+    want = oracle.gate_and_add(h, kv, qb, kb, 1e-6)
+    e = relerr(got, want)
+    log(f"  relerr {e:.2e}")
+    assert e <= 2e-3
+    # value = 0 leaves h bit for bit
+    kv0 = kv.reshape(T, hc + 1, dim).copy()
+    kv0[:, hc] = 0
+    d_h = torch.from_numpy(h).cuda()
+    E.gate_apply(d_h, cuda(kv0.reshape(T, -1)), d_qk, 1e-6)
+    np.testing.assert_array_equal(d_h.cpu().numpy().view(np.uint32), h.view(np.uint32))
