@@ -247,6 +247,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="run only the prefill measurement (for counter passes)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain elementwise copy of BYTES bytes (read BYTES, write "
+                         "BYTES) three times: the calibration kernel for the HBM counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -263,6 +268,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "kernel": "torch.neg float32, 3 launches"}))
+        return
+    if args.no_decode:
+        print(json.dumps({"prefill": bench_prefill(args, torch, E, G, synth)}), flush=True)
+        return
     dec = bench_decode(args, torch, E, G, synth)
     log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
     pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)

@@ -127,6 +127,8 @@ int32_t check_project(const uint16_t *x, const uint16_t *w, const uint16_t *y, i
     CHECK(T * K < kMaxElems && N * K < kMaxElems && T * N < ((int64_t)1 << 40), ENGRAM_E_UNSUPPORTED,
           "engram project: operands of %lld x %lld x %lld exceed 2^31 elements", (long long)T,
           (long long)K, (long long)N);
+    if (T == 0)
+        return ENGRAM_OK;                 // nothing to read or write
     CHECK(x && w && y, ENGRAM_E_ARG, "engram project: NULL pointer");
     CHECK(aligned(x, 16) && aligned(w, 16) && aligned(y, 16), ENGRAM_E_ARG,
           "engram project: x, w, y must be 16-byte aligned");
@@ -152,6 +154,8 @@ int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t 
     CHECK(dim >= 256 && dim % 256 == 0 && dim <= (1 << 20), ENGRAM_E_UNSUPPORTED,
           "engram gate: dim = %lld must be a multiple of 256", (long long)dim);
     CHECK(std::isfinite(eps) && eps >= 0.0f, ENGRAM_E_ARG, "engram gate: eps = %g", (double)eps);
+    if (T == 0)
+        return ENGRAM_OK;
     CHECK(h && kv && qk, ENGRAM_E_ARG, "engram gate: NULL pointer");
     CHECK(aligned(h, 16) && aligned(kv, 8) && aligned(qk, 16), ENGRAM_E_ARG,
           "engram gate: h and qk must be 16-byte, kv 8-byte aligned");

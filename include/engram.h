@@ -22,6 +22,8 @@
  *     argument check runs on the host before any launch; a refused call
  *     enqueues nothing and leaves every buffer untouched.  engram_last_error()
  *     returns the message of the calling thread's last failure.
+ *   - A stateless call with T = 0 checks its sizes and returns ENGRAM_OK
+ *     without touching memory; its array pointers may then be NULL.
  *   - Errors only the device can see (a token id outside the vocabulary, a
  *     row id outside the table) are recorded in a caller-supplied int32
  *     error word (d_err, nullable) as a bit mask of ENGRAM_DEVERR_*; the
