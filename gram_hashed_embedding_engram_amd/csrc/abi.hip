@@ -136,13 +136,13 @@ int32_t check_project(const uint16_t *x, const uint16_t *w, const uint16_t *y, i
 }
 
 int32_t dispatch_project(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
-                         int64_t N, hipStream_t s)
+                         int64_t N, const Launch &l)
 {
     if (T == 0)
         return ENGRAM_OK;
     if (T <= kGemvMaxT && K <= kGemvMaxK)
-        return launch_gemv(x, w, y, T, K, N, s);
-    return launch_gemm(x, w, y, T, K, N, s);
+        return launch_gemv(x, w, y, T, K, N, l);
+    return launch_gemm(x, w, y, T, K, N, l);
 }
 
 int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
@@ -240,20 +240,29 @@ hipEvent_t take_event(engram_ctx *ctx)
     return e;
 }
 
-// Runs one stage's launch, bracketed by events when timing is on.
+// Runs one stage's launch on stream s; with timing on, the runtime records a
+// pair of events with the stage's kernel dispatch itself.
 template <class F>
 int32_t staged(engram_ctx *ctx, int stage, hipStream_t s, F &&launch)
 {
+    Launch l;
+    l.stream = s;
     if (!ctx->timing)
-        return launch();
-    hipEvent_t a = take_event(ctx), b = take_event(ctx);
-    if (!a || !b)
+        return launch(l);
+    l.start = take_event(ctx);
+    l.stop = take_event(ctx);
+    if (!l.start || !l.stop)
         return fail(ENGRAM_E_HIP, "engram timing: hipEventCreate failed");
-    (void)hipEventRecord(a, s);
-    const int32_t rc = launch();
-    (void)hipEventRecord(b, s);
-    ctx->recs.push_back({stage, a, b});
+    const int32_t rc = launch(l);
+    ctx->recs.push_back({stage, l.start, l.stop});
     return rc;
+}
+
+Launch on(void *stream)
+{
+    Launch l;
+    l.stream = as_stream(stream);
+    return l;
 }
 
 }  // namespace
@@ -283,7 +292,7 @@ int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int6
         return ENGRAM_OK;
     CHECK(d_ids && d_history && d_row_ids, ENGRAM_E_ARG, "engram hash: NULL pointer");
     return launch_hash(c, tables->d_token_map, d_ids, T, start_pos, d_history, d_row_ids, d_err,
-                       as_stream(stream));
+                       on(stream));
 }
 
 int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_ids, int64_t T,
@@ -301,7 +310,7 @@ int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_id
     CHECK(d_row_ids && d_rows, ENGRAM_E_ARG, "engram gather: NULL pointer");
     CHECK(aligned(d_rows, 16) && aligned(d_row_ids, 8), ENGRAM_E_ARG,
           "engram gather: rows must be 16-byte, ids 8-byte aligned");
-    return launch_gather(*table, d_row_ids, T, cols, id_stride, d_rows, d_err, as_stream(stream));
+    return launch_gather(*table, d_row_ids, T, cols, id_stride, d_rows, d_err, on(stream));
 }
 
 int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
@@ -310,7 +319,7 @@ int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, 
     int32_t rc = check_project(d_x, d_w, d_y, T, K, N);
     if (rc != ENGRAM_OK)
         return rc;
-    return dispatch_project(d_x, d_w, d_y, T, K, N, as_stream(stream));
+    return dispatch_project(d_x, d_w, d_y, T, K, N, on(stream));
 }
 
 int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk, int64_t n,
@@ -320,7 +329,7 @@ int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk,
     if (n == 0)
         return ENGRAM_OK;
     CHECK(d_q && d_k && d_qk, ENGRAM_E_ARG, "engram qk: NULL pointer");
-    return launch_qk_product(d_q, d_k, d_qk, n, as_stream(stream));
+    return launch_qk_product(d_q, d_k, d_qk, n, on(stream));
 }
 
 int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, int64_t T,
@@ -329,7 +338,7 @@ int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, i
     int32_t rc = check_gate(d_h, d_kv, d_qk, T, hc, dim, eps);
     if (rc != ENGRAM_OK)
         return rc;
-    return launch_gate(d_h, d_kv, d_qk, T, hc, dim, eps, as_stream(stream));
+    return launch_gate(d_h, d_kv, d_qk, T, hc, dim, eps, on(stream));
 }
 
 size_t engram_workspace_bytes(const engram_config *cfg)
@@ -419,10 +428,10 @@ int32_t engram_ctx_add_layer(engram_ctx *ctx, int32_t hash_index, const engram_t
 int32_t engram_reset(engram_ctx *ctx, void *stream)
 {
     CHECK(ctx, ENGRAM_E_ARG, "engram reset: NULL context");
-    hipStream_t s = as_stream(stream);
-    int32_t rc = launch_fill_zero(ctx->history, sizeof(int64_t) * (size_t)ctx->cfg.max_seq, s);
+    const Launch l = on(stream);
+    int32_t rc = launch_fill_zero(ctx->history, sizeof(int64_t) * (size_t)ctx->cfg.max_seq, l);
     if (rc == ENGRAM_OK)
-        rc = launch_fill_zero(ctx->err, 256, s);
+        rc = launch_fill_zero(ctx->err, 256, l);
     if (rc != ENGRAM_OK)
         return rc;
     ctx->pos = 0;
@@ -460,9 +469,9 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     int32_t rc;
     if (hash_index == 0) {
         const int64_t start = ctx->pos;
-        rc = staged(ctx, 0, s, [&] {
+        rc = staged(ctx, 0, s, [&](const Launch &l) {
             return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, T, start, ctx->history,
-                               ctx->row_ids, ctx->err, s);
+                               ctx->row_ids, ctx->err, l);
         });
         if (rc != ENGRAM_OK)
             return rc;
@@ -471,19 +480,19 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
         ctx->step_T = T;
     }
     const int64_t K = (int64_t)ctx->cols * cfg.head_dim;
-    rc = staged(ctx, 1, s, [&] {
+    rc = staged(ctx, 1, s, [&](const Launch &l) {
         return launch_gather(L.tab, ctx->row_ids + (int64_t)hash_index * ctx->cols, T, ctx->cols,
-                             (int64_t)ctx->nl * ctx->cols, ctx->rows, ctx->err, s);
+                             (int64_t)ctx->nl * ctx->cols, ctx->rows, ctx->err, l);
     });
     if (rc != ENGRAM_OK)
         return rc;
-    rc = staged(ctx, 2, s, [&] {
-        return dispatch_project(ctx->rows, L.wkv, ctx->kv, T, K, ctx->kv_width, s);
+    rc = staged(ctx, 2, s, [&](const Launch &l) {
+        return dispatch_project(ctx->rows, L.wkv, ctx->kv, T, K, ctx->kv_width, l);
     });
     if (rc != ENGRAM_OK)
         return rc;
-    return staged(ctx, 3, s, [&] {
-        return launch_gate(d_h, ctx->kv, L.qk, T, cfg.hc, cfg.dim, cfg.eps, s);
+    return staged(ctx, 3, s, [&](const Launch &l) {
+        return launch_gate(d_h, ctx->kv, L.qk, T, cfg.hc, cfg.dim, cfg.eps, l);
     });
 }
 

@@ -2,6 +2,7 @@
 // reductions and the host-side launch helpers.  Internal to the library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,6 +49,23 @@ int32_t launch_status(const char *what);
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Where a launcher enqueues: the stream, and optionally a pair of events the
+// runtime records with the dispatch of the launcher's first kernel and the
+// completion of its last (stage timing; null events = a plain launch).
+struct Launch {
+    hipStream_t stream = nullptr;
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <class F, class... Args>
+inline void dispatch(F kernel, dim3 grid, dim3 block, const Launch &l, bool first, bool last,
+                     Args... args)
+{
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, l.stream, first ? l.start : nullptr,
+                          last ? l.stop : nullptr, 0, args...);
+}
+
 // Hash constants, passed by value as a kernel argument.
 struct HashConsts {
     int32_t nl, ng, nh, cols;
@@ -61,18 +79,18 @@ struct HashConsts {
 // the caller; these only enqueue.
 int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t T,
                     int64_t start_pos, int64_t *history, int64_t *row_ids, int32_t *err,
-                    hipStream_t s);
+                    const Launch &l);
 int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T, int32_t cols,
-                      int64_t id_stride, uint16_t *rows, int32_t *err, hipStream_t s);
+                      int64_t id_stride, uint16_t *rows, int32_t *err, const Launch &l);
 int32_t launch_gemv(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
-                    int64_t N, hipStream_t s);
+                    int64_t N, const Launch &l);
 int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t K,
-                    int64_t N, hipStream_t s);
+                    int64_t N, const Launch &l);
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
-                    int64_t dim, float eps, hipStream_t s);
+                    int64_t dim, float eps, const Launch &l);
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
-                          hipStream_t s);
-int32_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+                          const Launch &l);
+int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
 
 // GEMV covers T <= kGemvMaxT with K <= kGemvMaxK; larger T goes to the GEMM.
 constexpr int64_t kGemvMaxT = 4;

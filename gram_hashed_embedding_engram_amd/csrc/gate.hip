@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 }  // namespace
 
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
-                    int64_t dim, float eps, hipStream_t s)
+                    int64_t dim, float eps, const Launch &l)
 {
     const int64_t waves = T * hc;
     if (waves == 0)
@@ -156,8 +156,8 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
     const bool in_registers = nch == 1 || nch == 2 || nch == 4 || nch == 8 || nch == 16;
 #define ENGRAM_GATE_CASE(N_)                                                              \
     case N_:                                                                              \
-        hipLaunchKernelGGL((gate_kernel<N_>), grid, block, 0, s, h, kv, qk, T, hc, dim, eps, \
-                           fdim, inv_sqrt_dim);                                          \
+        dispatch(gate_kernel<N_>, grid, block, l, true, true, h, kv, qk, T, hc, dim, eps, fdim, \
+                 inv_sqrt_dim);                                                          \
         break;
     if (in_registers) {
         switch (nch) {
@@ -167,26 +167,26 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
             break;
         }
     } else {
-        hipLaunchKernelGGL(gate_kernel_2pass, grid, block, 0, s, h, kv, qk, T, hc, dim, eps,
-                           fdim, inv_sqrt_dim);
+        dispatch(gate_kernel_2pass, grid, block, l, true, true, h, kv, qk, T, hc, dim, eps, fdim,
+                 inv_sqrt_dim);
     }
 #undef ENGRAM_GATE_CASE
     return launch_status("engram gate kernel");
 }
 
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
-                          hipStream_t s)
+                          const Launch &l)
 {
     if (n == 0)
         return ENGRAM_OK;
     int64_t blocks = (n + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;
-    hipLaunchKernelGGL(qk_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q, k, qk, n);
+    dispatch(qk_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, q, k, qk, n);
     return launch_status("engram qk kernel");
 }
 
-int32_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
+int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l)
 {
     const int64_t words = (int64_t)(bytes / 4);
     if (words == 0)
@@ -194,8 +194,8 @@ int32_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
     int64_t blocks = (words + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p,
-                       words);
+    dispatch(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, (uint32_t *)p,
+             words);
     return launch_status("engram fill kernel");
 }
 

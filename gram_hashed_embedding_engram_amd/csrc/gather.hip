@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void gather_e4m3_kernel(const uint8_t *__restr
 }  // namespace
 
 int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T, int32_t cols,
-                      int64_t id_stride, uint16_t *rows, int32_t *err, hipStream_t s)
+                      int64_t id_stride, uint16_t *rows, int32_t *err, const Launch &l)
 {
     const int64_t total_rows = T * cols;
     if (total_rows == 0)
@@ -179,16 +179,16 @@ int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T
         int64_t blocks = (total_rows + kQ2kRows - 1) / kQ2kRows;
         if (blocks > 16384)
             blocks = 16384;
-        hipLaunchKernelGGL(gather_q2k_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tab.d_data,
-                           tab.n_rows, row_ids, id_stride, cols, total_rows, rows, err);
+        dispatch(gather_q2k_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, tab.d_data,
+                 tab.n_rows, row_ids, id_stride, cols, total_rows, rows, err);
     } else {
         const int64_t threads = total_rows * (tab.head_dim / 16);
         int64_t blocks = (threads + 255) / 256;
         if (blocks > 16384)
             blocks = 16384;
-        hipLaunchKernelGGL(gather_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           tab.d_data, tab.d_scales, tab.n_rows, tab.head_dim, tab.scale_block,
-                           row_ids, id_stride, cols, total_rows, rows, err);
+        dispatch(gather_e4m3_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, tab.d_data,
+                 tab.d_scales, tab.n_rows, tab.head_dim, tab.scale_block, row_ids, id_stride, cols,
+                 total_rows, rows, err);
     }
     return launch_status("engram gather kernel");
 }

@@ -46,13 +46,18 @@ constexpr int XCDS = 8;
 
 __device__ __forceinline__ int swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+typedef __attribute__((address_space(1))) const void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+
+constexpr int TILE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per buffer (64 KiB)
+
 __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ A,
                                                    const uint16_t *__restrict__ B,
                                                    uint16_t *__restrict__ C, int M, int N, int K,
                                                    int tiles_m, int tiles_n)
 {
-    __shared__ u32x4 sA[2][BM * KCH];
-    __shared__ u32x4 sB[2][BN * KCH];
+    // [buffer][256 token rows, then 256 wkv rows][8 chunks]
+    __shared__ u32x4 smem[2][TILE_SLOTS];
 
     // ---- tile of this workgroup: XCD-contiguous ranges, grouped raster
     const int G = tiles_m * tiles_n;
@@ -70,21 +75,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
 
-    // ---- global -> register mapping: chunk (row = 32*j + tid/8, c = tid%8)
-    const int lrow = tid >> 3, lc = tid & 7;
-    const int kc = K >> 3;                          // 16-byte chunks per matrix row
-    const u32x4 *A4 = (const u32x4 *)A;
-    const u32x4 *B4 = (const u32x4 *)B;
-    uint32_t aoff[8], boff[8];
-    int sidx[8];
+    // ---- loader: each wave fills 64 rows of the token tile and 64 rows of
+    // the wkv tile, 8 rows (1 KiB) per direct-to-LDS load.  A load writes
+    // lane l's 16 bytes to LDS slot l of its 64-slot block, so lane l takes
+    // row 8j + l/8 of the block and the global chunk that belongs in LDS
+    // slot l%8 of that row under the swizzle.
+    const int lrow = lane >> 3, lslot = lane & 7;
+    int aoff[8], boff[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const int row = 32 * j + lrow;
-        const int am = min(m0 + row, M - 1), bn = min(n0 + row, N - 1);
-        aoff[j] = (uint32_t)am * (uint32_t)kc + lc;
-        boff[j] = (uint32_t)bn * (uint32_t)kc + lc;
-        sidx[j] = row * KCH + (lc ^ swizzle(row));
+        const int row = wave * 64 + 8 * j + lrow;
+        const int chunk = lslot ^ swizzle(row);
+        aoff[j] = min(m0 + row, M - 1) * K + chunk * 8;
+        boff[j] = min(n0 + row, N - 1) * K + chunk * 8;
     }
+    auto issue_loads = [&](int kt, int buf) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            __builtin_amdgcn_global_load_lds((gptr_t)(A + aoff[j] + k0),
+                                             (lptr_t)&smem[buf][(wave * 64 + 8 * j) * KCH], 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds((gptr_t)(B + boff[j] + k0),
+                                             (lptr_t)&smem[buf][(BM + wave * 64 + 8 * j) * KCH],
+                                             16, 0, 0);
+        }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -95,59 +111,73 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
             for (int e = 0; e < 16; e++)
                 acc[i][j][e] = 0.0f;
 
-    u32x4 ra[8], rb[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        ra[j] = A4[aoff[j]];
-        rb[j] = B4[boff[j]];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        sA[0][sidx[j]] = ra[j];
-        sB[0][sidx[j]] = rb[j];
-    }
-    __syncthreads();
-
     // fragment rows of this lane: 32-row blocks, row within block = lane % 32
     const int fr = lane & 31, fhalf = lane >> 5;
     const int fsw = swizzle(fr);
+    auto read_frags = [&](int buf, int kk, bf16x8 *fa, bf16x8 *fb) {
+        const int ch = (2 * kk + fhalf) ^ fsw;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            fa[i] = __builtin_bit_cast(bf16x8,
+                                       smem[buf][(BM + wn * 128 + i * 32 + fr) * KCH + ch]);
+            fb[i] = __builtin_bit_cast(bf16x8, smem[buf][(wm * 128 + i * 32 + fr) * KCH + ch]);
+        }
+    };
+
+    // Pipeline of one K step (4 sub-steps of 16): the next step's tiles are
+    // requested first (direct to the other LDS buffer); sub-step kk's 16 MFMAs
+    // run while sub-step kk+1's fragments are read, one LDS read interleaved
+    // after each MFMA; before the last sub-step the workgroup meets at the
+    // barrier (the next tiles have landed, every wave is done with this
+    // buffer) and the next step's first fragments are read behind the last
+    // sub-step's MFMAs.
+    issue_loads(0, 0);
+    __syncthreads();
+    bf16x8 fa[2][4], fb[2][4];
+    read_frags(0, 0, fa[0], fb[0]);
     const int KT = K / BK;
     for (int kt = 0; kt < KT; kt++) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) {
-            const uint32_t adv = (uint32_t)(kt + 1) * KCH;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                ra[j] = A4[aoff[j] + adv];
-                rb[j] = B4[boff[j] + adv];
-            }
-        }
+        // the last step reloads its own tile into the idle buffer instead of
+        // branching, so the loop body stays one block the scheduler can
+        // interleave (the extra tile is never read)
+        issue_loads(min(kt + 1, KT - 1), cur ^ 1);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
-            const int ch = (2 * kk + fhalf) ^ fsw;
-            bf16x8 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int rn = wn * 128 + i * 32 + fr;
-                fa[i] = __builtin_bit_cast(bf16x8, sB[cur][rn * KCH + ch]);
-                const int rm = wm * 128 + i * 32 + fr;
-                fb[i] = __builtin_bit_cast(bf16x8, sA[cur][rm * KCH + ch]);
+            if (kk + 1 < BK / 16) {
+                read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            } else {
+                __syncthreads();
+                read_frags(cur ^ 1, 0, fa[0], fb[0]);
             }
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
-                                                                        0, 0, 0);
-        }
-        if (kt + 1 < KT) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+            if (kk == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                sA[cur ^ 1][sidx[j]] = ra[j];
-                sB[cur ^ 1][sidx[j]] = rb[j];
+                for (int r = 0; r < 8; r++) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global->LDS load
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                }
+#pragma unroll
+                for (int r = 0; r < 8; r++) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; r++) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);      // one sub-step per scheduling region
         }
-        __syncthreads();
     }
 
     // ---- epilogue: accumulator e of block (i, j) is output
@@ -178,14 +208,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
 }  // namespace
 
 int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t K,
-                    int64_t N, hipStream_t s)
+                    int64_t N, const Launch &l)
 {
     if (M == 0)
         return ENGRAM_OK;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
-    hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, s, x, w, y, (int)M,
-                       (int)N, (int)K, tiles_m, tiles_n);
+    dispatch(gemm_kernel, dim3((unsigned)tiles), dim3(256), l, true, true, x, w, y, (int)M, (int)N,
+             (int)K, tiles_m, tiles_n);
     return launch_status("engram gemm kernel");
 }
 

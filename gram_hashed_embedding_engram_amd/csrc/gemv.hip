@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ 
 
 template <int NT>
 int32_t launch_nt(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, int64_t N,
-                  hipStream_t s)
+                  const Launch &l, bool first, bool last)
 {
     static int cus = 0;
     if (cus == 0) {
@@ -102,7 +102,7 @@ int32_t launch_nt(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, 
     const dim3 grid((unsigned)blocks), block(256);
 #define ENGRAM_GEMV_CASE(NI_)                                                               \
     case NI_:                                                                               \
-        hipLaunchKernelGGL((gemv_kernel<NT, NI_>), grid, block, 0, s, x, w, y, K, N);       \
+        dispatch(gemv_kernel<NT, NI_>, grid, block, l, first, last, x, w, y, K, N);         \
         break;
     switch (ni) {
         ENGRAM_GEMV_CASE(1) ENGRAM_GEMV_CASE(2) ENGRAM_GEMV_CASE(3) ENGRAM_GEMV_CASE(4)
@@ -120,14 +120,16 @@ int32_t launch_nt(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, 
 }  // namespace
 
 int32_t launch_gemv(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
-                    int64_t N, hipStream_t s)
+                    int64_t N, const Launch &l)
 {
     // two tokens share one pass over the weights; a third or fourth token
     // takes another pass
     for (int64_t t0 = 0; t0 < T; t0 += 2) {
         const int64_t nt = T - t0 >= 2 ? 2 : 1;
-        const int32_t rc = nt == 2 ? launch_nt<2>(x + t0 * K, w, y + t0 * N, K, N, s)
-                                   : launch_nt<1>(x + t0 * K, w, y + t0 * N, K, N, s);
+        const bool first = t0 == 0, last = t0 + nt >= T;
+        const int32_t rc = nt == 2
+                               ? launch_nt<2>(x + t0 * K, w, y + t0 * N, K, N, l, first, last)
+                               : launch_nt<1>(x + t0 * K, w, y + t0 * N, K, N, l, first, last);
         if (rc != ENGRAM_OK)
             return rc;
     }

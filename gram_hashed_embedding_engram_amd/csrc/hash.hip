@@ -96,14 +96,14 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashConsts c,
 
 int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t T,
                     int64_t start_pos, int64_t *history, int64_t *row_ids, int32_t *err,
-                    hipStream_t s)
+                    const Launch &l)
 {
     const int64_t threads = T * c.nl * c.nh;
     if (threads == 0)
         return ENGRAM_OK;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(256), 0, s, c, token_map, ids,
-                       T, start_pos, history, row_ids, err);
+    dispatch(hash_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, c, token_map, ids, T,
+             start_pos, history, row_ids, err);
     return launch_status("engram hash kernel");
 }
 
