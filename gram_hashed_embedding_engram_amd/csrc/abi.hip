@@ -124,9 +124,11 @@ int32_t check_project(const uint16_t *x, const uint16_t *w, const uint16_t *y, i
           "engram project: K = %lld must be a positive multiple of 64", (long long)K);
     CHECK(N >= 16 && N % 16 == 0, ENGRAM_E_UNSUPPORTED,
           "engram project: N = %lld must be a positive multiple of 16", (long long)N);
-    CHECK(T * K < kMaxElems && N * K < kMaxElems && T * N < ((int64_t)1 << 40), ENGRAM_E_UNSUPPORTED,
-          "engram project: operands of %lld x %lld x %lld exceed 2^31 elements", (long long)T,
-          (long long)K, (long long)N);
+    // the GEMM addresses each operand with 32-bit byte offsets, tile tails
+    // (up to 255 rows past the end) included
+    CHECK((T + 256) * K < kMaxElems && (N + 256) * K < kMaxElems && T * N < ((int64_t)1 << 40),
+          ENGRAM_E_UNSUPPORTED, "engram project: operands of %lld x %lld x %lld exceed 2^31 elements",
+          (long long)T, (long long)K, (long long)N);
     if (T == 0)
         return ENGRAM_OK;                 // nothing to read or write
     CHECK(x && w && y, ENGRAM_E_ARG, "engram project: NULL pointer");
@@ -370,7 +372,7 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
     const int64_t K = (int64_t)c.cols * cfg->head_dim, N = cfg->dim * (cfg->hc + 1);
     CHECK(K % 64 == 0, ENGRAM_E_UNSUPPORTED, "engram ctx: cols*head_dim = %lld not a multiple of 64",
           (long long)K);
-    CHECK(cfg->max_tokens * K < kMaxElems && N * K < kMaxElems, ENGRAM_E_UNSUPPORTED,
+    CHECK((cfg->max_tokens + 256) * K < kMaxElems && (N + 256) * K < kMaxElems, ENGRAM_E_UNSUPPORTED,
           "engram ctx: projection operands exceed 2^31 elements");
     Carve cv;
     carve(cfg, &cv);

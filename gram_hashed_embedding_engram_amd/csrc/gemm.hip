@@ -39,25 +39,38 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256;            // tokens per tile
 constexpr int BN = 256;            // outputs per tile
-constexpr int BK = 64;             // K per step
-constexpr int KCH = BK / 8;        // 16-byte chunks per tile row
+constexpr int BK = 32;             // K per pipeline stage
+constexpr int KCH = BK / 8;        // 16-byte chunks per tile row (4)
+constexpr int NSTAGE = 4;          // LDS stages: 3 tiles in flight ahead of the one in use
 constexpr int GROUP_M = 4;         // token tiles walked per wkv tile
 constexpr int XCDS = 8;
+constexpr int LOADS = 4;           // 1 KiB direct loads per wave per operand per stage
 
-__device__ __forceinline__ int swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-typedef __attribute__((address_space(1))) const void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
 
-constexpr int TILE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per buffer (64 KiB)
+constexpr int STAGE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per stage (32 KiB)
+
+// LDS position of 16-byte chunk c of tile row r: c ^ swizzle(r).  For any 16
+// consecutive rows at one chunk, the rows sharing r % 4 (one 256-byte bank
+// line) land on 4 different positions, and so do the rows sharing r % 2
+// within any 8, so 16-byte fragment reads of consecutive rows hit distinct
+// banks whether a pass serves 8 or 16 lanes.
+__device__ __forceinline__ int swizzle(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+
+// Wait until at most `pending` of this wave's global->LDS loads are still in
+// flight (they complete in issue order) and its LDS reads are done, then
+// meet the workgroup.  Written out because __syncthreads would also wait for
+// the loads of the stages still being prefetched.
+#define ENGRAM_STAGE_BARRIER(pending)                                                       \
+    asm volatile("s_waitcnt vmcnt(" #pending ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ A,
                                                    const uint16_t *__restrict__ B,
                                                    uint16_t *__restrict__ C, int M, int N, int K,
                                                    int tiles_m, int tiles_n)
 {
-    // [buffer][256 token rows, then 256 wkv rows][8 chunks]
-    __shared__ u32x4 smem[2][TILE_SLOTS];
+    // [stage][256 token rows, then 256 wkv rows][4 chunks]
+    __shared__ u32x4 smem[NSTAGE][STAGE_SLOTS];
 
     // ---- tile of this workgroup: XCD-contiguous ranges, grouped raster
     const int G = tiles_m * tiles_n;
@@ -76,30 +89,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     const int wm = wave & 1, wn = wave >> 1;
 
     // ---- loader: each wave fills 64 rows of the token tile and 64 rows of
-    // the wkv tile, 8 rows (1 KiB) per direct-to-LDS load.  A load writes
-    // lane l's 16 bytes to LDS slot l of its 64-slot block, so lane l takes
-    // row 8j + l/8 of the block and the global chunk that belongs in LDS
-    // slot l%8 of that row under the swizzle.
-    const int lrow = lane >> 3, lslot = lane & 7;
-    int aoff[8], boff[8];
+    // the wkv tile, 16 rows (1 KiB) per direct-to-LDS buffer load.  A load
+    // writes lane l's 16 bytes to LDS slot l of its 64-slot block, so lane l
+    // takes row 16j + l/4 of the block and the global chunk that belongs in
+    // slot l%4 of that row under the swizzle.  The buffer descriptors bound
+    // each operand, so rows past M or N read as zeros; the K position of a
+    // stage travels in the scalar offset.  (Buffer loads count only in the
+    // vector-memory counter, so waiting for LDS reads never waits for them.)
+    const __amdgpu_buffer_rsrc_t rsA =
+        __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, (int)((uint32_t)M * K * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc((void *)B, 0, (int)((uint32_t)N * K * 2), 0x00020000);
+    const int lrow = lane >> 2, lslot = lane & 3;
+    uint32_t aoff[LOADS], boff[LOADS];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int row = wave * 64 + 8 * j + lrow;
+    for (int j = 0; j < LOADS; j++) {
+        const int row = wave * 64 + 16 * j + lrow;
         const int chunk = lslot ^ swizzle(row);
-        aoff[j] = min(m0 + row, M - 1) * K + chunk * 8;
-        boff[j] = min(n0 + row, N - 1) * K + chunk * 8;
+        aoff[j] = ((uint32_t)(m0 + row) * K + chunk * 8) * 2;
+        boff[j] = ((uint32_t)(n0 + row) * K + chunk * 8) * 2;
     }
-    auto issue_loads = [&](int kt, int buf) {
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            __builtin_amdgcn_global_load_lds((gptr_t)(A + aoff[j] + k0),
-                                             (lptr_t)&smem[buf][(wave * 64 + 8 * j) * KCH], 16,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds((gptr_t)(B + boff[j] + k0),
-                                             (lptr_t)&smem[buf][(BM + wave * 64 + 8 * j) * KCH],
-                                             16, 0, 0);
-        }
+    const int KT = K / BK;
+    // one 1 KiB direct load: q = 0..7 -> operand q&1 (token / wkv), block q>>1
+    auto load_one = [&](int kt, int q) {
+        // past the end: reload the last tile (never read)
+        const uint32_t kbytes = (uint32_t)min(kt, KT - 1) * BK * 2;
+        const int st = kt % NSTAGE;
+        const int j = q >> 1;
+        if ((q & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsA, (lptr_t)&smem[st][(wave * 64 + 16 * j) * KCH], 16, aoff[j], kbytes, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsB, (lptr_t)&smem[st][(BM + wave * 64 + 16 * j) * KCH], 16, boff[j], kbytes, 0,
+                0);
     };
 
     f32x16 acc[4][4];
@@ -114,71 +137,67 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
     // fragment rows of this lane: 32-row blocks, row within block = lane % 32
     const int fr = lane & 31, fhalf = lane >> 5;
     const int fsw = swizzle(fr);
-    auto read_frags = [&](int buf, int kk, bf16x8 *fa, bf16x8 *fb) {
+    // fragment f of a sub-step: f < 4 -> wkv rows block f ("A" operand),
+    // f >= 4 -> token rows block f-4 ("B" operand)
+    auto read_one = [&](int st, int kk, int f) -> bf16x8 {
         const int ch = (2 * kk + fhalf) ^ fsw;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            fa[i] = __builtin_bit_cast(bf16x8,
-                                       smem[buf][(BM + wn * 128 + i * 32 + fr) * KCH + ch]);
-            fb[i] = __builtin_bit_cast(bf16x8, smem[buf][(wm * 128 + i * 32 + fr) * KCH + ch]);
-        }
+        const int row = f < 4 ? BM + wn * 128 + f * 32 + fr : wm * 128 + (f - 4) * 32 + fr;
+        return __builtin_bit_cast(bf16x8, smem[st][row * KCH + ch]);
     };
 
-    // Pipeline of one K step (4 sub-steps of 16): the next step's tiles are
-    // requested first (direct to the other LDS buffer); sub-step kk's 16 MFMAs
-    // run while sub-step kk+1's fragments are read, one LDS read interleaved
-    // after each MFMA; before the last sub-step the workgroup meets at the
-    // barrier (the next tiles have landed, every wave is done with this
-    // buffer) and the next step's first fragments are read behind the last
-    // sub-step's MFMAs.
-    issue_loads(0, 0);
-    __syncthreads();
-    bf16x8 fa[2][4], fb[2][4];
-    read_frags(0, 0, fa[0], fb[0]);
-    const int KT = K / BK;
+    // Pipeline.  Tiles kt+1..kt+3 are in flight while tile kt is used.  A tile
+    // is two sub-steps of 16 MFMAs.  Each sub-step is issued as 8 groups of
+    // 2 MFMAs + 1 LDS read of the next sub-step's fragments, with one of the
+    // next tile's 8 direct loads in every other group: memory instructions
+    // trickle between matrix-core instructions instead of arriving in a burst
+    // that would stall the in-order issue of the MFMAs behind them.  Before a
+    // tile's second sub-step the workgroup meets: tile kt+1 has landed (at
+    // most 12 younger loads pending) and every wave is done with tile kt-1's
+    // stage, which this tile's prefetch overwrites.
+    bf16x8 f0[8], f1[8];
+    for (int q = 0; q < 8; q++)
+        load_one(0, q);
+    for (int q = 0; q < 8; q++)
+        load_one(1, q);
+    for (int q = 0; q < 8; q++)
+        load_one(2, q);
+    ENGRAM_STAGE_BARRIER(16);
+#pragma unroll
+    for (int f = 0; f < 8; f++)
+        f0[f] = read_one(0, 0, f);
     for (int kt = 0; kt < KT; kt++) {
-        const int cur = kt & 1;
-        // the last step reloads its own tile into the idle buffer instead of
-        // branching, so the loop body stays one block the scheduler can
-        // interleave (the extra tile is never read)
-        issue_loads(min(kt + 1, KT - 1), cur ^ 1);
+        const int st = kt % NSTAGE;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            if (kk + 1 < BK / 16) {
-                read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            } else {
-                __syncthreads();
-                read_frags(cur ^ 1, 0, fa[0], fb[0]);
-            }
+        for (int g = 0; g < 8; g++) {
+            const int i = g >> 1, j0 = 2 * (g & 1);
+            acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j0], acc[i][j0],
+                                                                 0, 0, 0);
+            acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                f0[i], f0[5 + j0], acc[i][j0 + 1], 0, 0, 0);
+            f1[g] = read_one(st, 1, g);
+            if ((g & 1) == 0)
+                load_one(kt + 3, g >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ENGRAM_STAGE_BARRIER(12);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nst = (kt + 1) % NSTAGE;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-            if (kk == 0) {
-#pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global->LDS load
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                }
-#pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);      // one sub-step per scheduling region
+        for (int g = 0; g < 8; g++) {
+            const int i = g >> 1, j0 = 2 * (g & 1);
+            acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j0], acc[i][j0],
+                                                                 0, 0, 0);
+            acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                f1[i], f1[5 + j0], acc[i][j0 + 1], 0, 0, 0);
+            f0[g] = read_one(nst, 0, g);
+            if ((g & 1) == 0)
+                load_one(kt + 3, 4 + (g >> 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // the trailing prefetches (reloads of the last tile) land before the
+    // workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: accumulator e of block (i, j) is output
     // n = 32i + 8(e/4) + 4(lane/32) + e%4 of this wave's 128 outputs, token
