@@ -41,7 +41,7 @@ constexpr int BM = 256;            // tokens per tile
 constexpr int BN = 256;            // outputs per tile
 constexpr int BK = 32;             // K per pipeline stage
 constexpr int KCH = BK / 8;        // 16-byte chunks per tile row (4)
-constexpr int NSTAGE = 4;          // LDS stages: 3 tiles in flight ahead of the one in use
+constexpr int NSTAGE = 4;          // LDS stages: NSTAGE-1 tiles in flight ahead of the one in use
 constexpr int GROUP_M = 4;         // token tiles walked per wkv tile
 constexpr int XCDS = 8;
 constexpr int LOADS = 4;           // 1 KiB direct loads per wave per operand per stage
@@ -49,6 +49,7 @@ constexpr int LOADS = 4;           // 1 KiB direct loads per wave per operand pe
 typedef __attribute__((address_space(3))) void *lptr_t;
 
 constexpr int STAGE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per stage (32 KiB)
+static_assert(NSTAGE >= 3 && NSTAGE * STAGE_SLOTS * 16 <= 160 * 1024, "LDS stages");
 
 // LDS position of 16-byte chunk c of tile row r: c ^ swizzle(r).  For any 16
 // consecutive rows at one chunk, the rows sharing r % 4 (one 256-byte bank
@@ -61,8 +62,11 @@ __device__ __forceinline__ int swizzle(int r) { return ((r >> 2) ^ (r >> 1)) & 3
 // flight (they complete in issue order) and its LDS reads are done, then
 // meet the workgroup.  Written out because __syncthreads would also wait for
 // the loads of the stages still being prefetched.
-#define ENGRAM_STAGE_BARRIER(pending)                                                       \
-    asm volatile("s_waitcnt vmcnt(" #pending ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+template <int PENDING>
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(PENDING) : "memory");
+}
 
 __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ A,
                                                    const uint16_t *__restrict__ B,
@@ -145,23 +149,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
         return __builtin_bit_cast(bf16x8, smem[st][row * KCH + ch]);
     };
 
-    // Pipeline.  Tiles kt+1..kt+3 are in flight while tile kt is used.  A tile
+    // Pipeline.  Tiles kt+1..kt+NSTAGE-1 are in flight while tile kt is used.  A tile
     // is two sub-steps of 16 MFMAs.  Each sub-step is issued as 8 groups of
     // 2 MFMAs + 1 LDS read of the next sub-step's fragments, with one of the
     // next tile's 8 direct loads in every other group: memory instructions
     // trickle between matrix-core instructions instead of arriving in a burst
     // that would stall the in-order issue of the MFMAs behind them.  Before a
-    // tile's second sub-step the workgroup meets: tile kt+1 has landed (at
-    // most 12 younger loads pending) and every wave is done with tile kt-1's
-    // stage, which this tile's prefetch overwrites.
+    // tile's second sub-step the workgroup meets: tile kt+1 has landed (the
+    // younger loads -- tiles kt+2.. and half of this tile's prefetch -- may
+    // still be pending) and every wave is done with tile kt-1's stage, which
+    // this tile's prefetch overwrites.
     bf16x8 f0[8], f1[8];
-    for (int q = 0; q < 8; q++)
-        load_one(0, q);
-    for (int q = 0; q < 8; q++)
-        load_one(1, q);
-    for (int q = 0; q < 8; q++)
-        load_one(2, q);
-    ENGRAM_STAGE_BARRIER(16);
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; t++)
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            load_one(t, q);
+    stage_barrier<(NSTAGE - 2) * 8>();
 #pragma unroll
     for (int f = 0; f < 8; f++)
         f0[f] = read_one(0, 0, f);
@@ -176,10 +180,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                 f0[i], f0[5 + j0], acc[i][j0 + 1], 0, 0, 0);
             f1[g] = read_one(st, 1, g);
             if ((g & 1) == 0)
-                load_one(kt + 3, g >> 1);
+                load_one(kt + NSTAGE - 1, g >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        ENGRAM_STAGE_BARRIER(12);
+        stage_barrier<(NSTAGE - 3) * 8 + 4>();
         __builtin_amdgcn_sched_barrier(0);
         const int nst = (kt + 1) % NSTAGE;
 #pragma unroll
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ 
                 f1[i], f1[5 + j0], acc[i][j0 + 1], 0, 0, 0);
             f0[g] = read_one(nst, 0, g);
             if ((g & 1) == 0)
-                load_one(kt + 3, 4 + (g >> 1));
+                load_one(kt + NSTAGE - 1, 4 + (g >> 1));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
