@@ -4,21 +4,23 @@
 
 Headline: the decode workload (two Q2_K engram layers, 32-token prompt, then
 single-token steps; wkv [20480, 6144] bf16 per layer).  One step = one token
-through both layers: hash, then per layer gather + dequant, projection (GEMV)
-and gate, all through engram_forward.  `value` = engram tokens/s per layer =
-steps * layers / seconds, inputs resident in HBM.
+through both layers via engram_forward: per layer one fused kernel (hash,
+gather + dequant of the token's 24 rows, projection) and the gate.  `value` =
+engram tokens/s per layer = steps * layers / seconds, inputs resident in HBM.
+The same steps through the staged kernels (hash, gather, GEMV, gate) are
+reported under "decode_staged".
 
 Also measured in the same run: the prefill workload (T = 4096 Zipf tokens,
 both layers, one hash pass; projection on the MFMA GEMM), reported under
 "prefill" with its own roofline.
 
-Per-kernel durations come from HIP events recorded by the library on the
-forward's stream around each stage (engram_ctx_set_timing) during a second
-pass over the same steps; the plain pass gives `value`.  The roofline uses the
-projection kernel: algorithmic bytes (decode GEMV) or flops (prefill GEMM)
-per launch divided by its average event-timed duration.  `traffic` is read
-from the committed rocprofv3 counter summary when it matches the current
-kernel source, else null.
+Per-kernel durations come from HIP events the runtime records with each
+kernel dispatch (engram_ctx_set_timing) during a second pass over the same
+steps; the plain pass gives `value`.  The roofline uses the projection
+kernel: algorithmic bytes (decode) or flops (prefill GEMM) per launch divided
+by its average event-timed duration.  `traffic` is read from the committed
+rocprofv3 counter summary when it matches the current kernel source, else
+null.
 
 The oracle (plain C on the host cores) is timed on a bounded sample of the
 same decode steps for `cpu_baseline`.
@@ -94,16 +96,28 @@ def make_ctx(E, w, tables, layers, max_tokens, max_seq):
     return ctx
 
 
-def bench_decode(args, torch, E, G, synth):
+def decode_bytes(w):
+    """Algorithmic bytes of one fused decode launch (one token, one layer):
+    wkv read once, the token's cols Q2_K blocks, kv written, the dequantised
+    rows and the step's row ids written back, the token id, its token-map
+    entry and max_ngram-1 history entries read, one history entry written."""
+    return (w.N * w.K * 2 + w.cols * 84 + w.N * 2 + w.K * 2 + w.n_layers * w.cols * 8
+            + 4 + 8 + 8 * w.max_ngram)
+
+
+def bench_decode(args, torch, E, G, synth, fused=True, inputs=None):
     w = synth.DECODE_Q2K
-    log(f"decode: generating {w.name}")
-    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    if inputs is None:
+        log(f"decode: generating {w.name}")
+        inputs = device_inputs(w, torch, E, G)
+    ht, tm, tables, layers, host = inputs
     n_tok = w.prompt + 2 * (args.warmup + args.steps)
     ids = G.token_ids(w, n_tok)
     d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
     hw = torch.from_numpy(G.highway(w, w.decode_steps, decode=True)).cuda()
     prompt_h = torch.from_numpy(G.highway(w, w.prompt)).cuda()
     ctx = make_ctx(E, w, tables, layers, w.prompt, n_tok)
+    ctx.set_fused_decode(fused)
     stream = torch.cuda.current_stream()
     nl = w.n_layers
     for l in range(nl):
@@ -135,21 +149,19 @@ def bench_decode(args, torch, E, G, synth):
     stages = ctx.timing()
     ctx.set_timing(False)
     ctx.check()
-    K, N = w.K, w.N
-    gemv_bytes = N * K * 2 + K * 2 + N * 2
-    gemv_ms, gemv_n = stages["project"]
-    gemv_avg = gemv_ms / gemv_n
-    gather_ms, gather_n = stages["gather"]
-    gather_bytes = w.cols * (84 + 512 + 8)
+    proj_ms, proj_n = stages["project"]
     res = dict(
+        fused=fused,
         ms_per_step=ms / args.steps,
         value=args.steps * nl / (ms / 1e3),
-        gemv_avg_ms=gemv_avg,
-        gemv_bytes=gemv_bytes,
-        stages={k: v[0] / max(1, v[1]) for k, v in stages.items()},
-        gather_GBps=gather_bytes / (gather_ms / gather_n / 1e3) / 1e9,
+        proj_avg_ms=proj_ms / proj_n,
+        proj_bytes=decode_bytes(w) if fused else w.N * w.K * 2 + w.K * 2 + w.N * 2,
+        stages={k: v[0] / max(1, v[1]) for k, v in stages.items() if v[1]},
         host=host, ht=ht, ids=ids,
     )
+    if not fused:
+        g_ms, g_n = stages["gather"]
+        res["gather_GBps"] = w.cols * (84 + 512 + 8) / (g_ms / g_n / 1e3) / 1e9
     del ctx
     return res
 
@@ -281,8 +293,13 @@ def main():
     if args.no_decode:
         print(json.dumps({"prefill": bench_prefill(args, torch, E, G, synth)}), flush=True)
         return
-    dec = bench_decode(args, torch, E, G, synth)
-    log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
+    inputs = device_inputs(synth.DECODE_Q2K, torch, E, G)
+    dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=inputs)
+    log(f"decode (fused): {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
+    staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=inputs)
+    log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
+        f"{staged['stages']}")
+    del inputs
     pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
     if pre:
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
@@ -291,7 +308,8 @@ def main():
         log("cpu baseline: oracle on the host cores")
         cpu = cpu_baseline(dec, synth, args.cpu_budget)
     w = synth.DECODE_Q2K
-    gbps = dec["gemv_bytes"] / (dec["gemv_avg_ms"] / 1e3) / 1e9
+    gbps = dec["proj_bytes"] / (dec["proj_avg_ms"] / 1e3) / 1e9
+    staged_gbps = staged["proj_bytes"] / (staged["proj_avg_ms"] / 1e3) / 1e9
     out = {
         "metric": "engram tokens/s per layer (decode T=1)",
         "value": dec["value"],
@@ -310,11 +328,16 @@ def main():
                        dec["ht"]["rows"][0]), "K": w.K, "N": w.N, "hc": w.hc, "dim": w.dim},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": counter_traffic("gemv_decode_counters.md", "gemv.hip"),
-                     "kernel": "gemv_kernel<1,12> (projection, one launch per layer-step)",
-                     "bytes_per_launch": dec["gemv_bytes"], "avg_launch_ms": dec["gemv_avg_ms"]},
+                     "traffic": counter_traffic("decode_kernel_counters.md", "decode.hip"),
+                     "kernel": "decode_kernel<Q2K,12> (hash + gather/dequant + projection of "
+                               "one layer for one token; one launch per layer-step)",
+                     "bytes_per_launch": dec["proj_bytes"], "avg_launch_ms": dec["proj_avg_ms"]},
         "stages_ms_per_layer_step": dec["stages"],
-        "gather_GBps": dec["gather_GBps"],
+        "decode_staged": {"ms_per_step": staged["ms_per_step"], "value": staged["value"],
+                          "stages_ms_per_layer_step": staged["stages"],
+                          "gemv_GBps": staged_gbps, "gather_GBps": staged["gather_GBps"],
+                          "gemv_traffic": counter_traffic("gemv_decode_counters.md",
+                                                          "gemv.hip")},
         "prefill": pre,
         "cpu_baseline": cpu,
     }

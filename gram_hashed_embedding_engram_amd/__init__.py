@@ -25,7 +25,8 @@ EXPORTS = (
     "engram_last_error", "engram_abi_version", "engram_hash", "engram_gather_dequant",
     "engram_project", "engram_qk_product", "engram_gate_apply", "engram_workspace_bytes",
     "engram_ctx_create", "engram_ctx_add_layer", "engram_reset", "engram_forward",
-    "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_timing",
+    "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
+    "engram_ctx_set_timing",
     "engram_ctx_timing", "engram_ctx_destroy",
 )
 
@@ -86,6 +87,7 @@ def lib():
             "engram_check": (i32, [p, p]),
             "engram_position": (i64, [p]),
             "engram_ctx_buffers": (i32, [p, p, p, p, p]),
+            "engram_ctx_set_fused_decode": (i32, [p, i32]),
             "engram_ctx_set_timing": (i32, [p, i32]),
             "engram_ctx_timing": (i32, [p, p, p]),
             "engram_ctx_destroy": (None, [p]),
@@ -249,6 +251,9 @@ class Context:
         return (view(rid, T * self.nl * self.cols, torch.int64, (T, self.nl, self.cols)),
                 view(rows, T * K, torch.int16, (T, K)),
                 view(kv, T * N, torch.int16, (T, N)))
+
+    def set_fused_decode(self, on: bool):
+        _check(lib().engram_ctx_set_fused_decode(self.h, 1 if on else 0))
 
     def set_timing(self, on: bool):
         _check(lib().engram_ctx_set_timing(self.h, 1 if on else 0))

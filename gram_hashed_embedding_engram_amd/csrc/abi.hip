@@ -194,6 +194,8 @@ struct engram_ctx {
     int64_t pos = 0;
     bool step_open = false;
     int64_t step_T = 0;
+    int64_t step_start = 0;
+    bool fused_decode = true;
     bool timing = false;
     std::vector<TimingRec> recs;
     std::vector<hipEvent_t> pool;
@@ -469,6 +471,25 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     hipStream_t s = as_stream(stream);
     const engram_config &cfg = ctx->cfg;
     int32_t rc;
+    // one decode token: hash, gather and projection in one launch
+    if (T == 1 && ctx->fused_decode && cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols) {
+        if (hash_index == 0) {
+            ctx->step_start = ctx->pos;
+            ctx->pos += 1;
+            ctx->step_open = true;
+            ctx->step_T = 1;
+        }
+        rc = staged(ctx, 2, s, [&](const Launch &l) {
+            return launch_decode(ctx->consts, cfg.hash.d_token_map, d_ids, ctx->step_start,
+                                 ctx->history, hash_index, hash_index == 0, L.tab, L.wkv, ctx->kv,
+                                 ctx->kv_width, ctx->row_ids, ctx->rows, ctx->err, l);
+        });
+        if (rc != ENGRAM_OK)
+            return rc;
+        return staged(ctx, 3, s, [&](const Launch &l) {
+            return launch_gate(d_h, ctx->kv, L.qk, 1, cfg.hc, cfg.dim, cfg.eps, l);
+        });
+    }
     if (hash_index == 0) {
         const int64_t start = ctx->pos;
         rc = staged(ctx, 0, s, [&](const Launch &l) {
@@ -477,6 +498,7 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
         });
         if (rc != ENGRAM_OK)
             return rc;
+        ctx->step_start = ctx->pos;
         ctx->pos += T;
         ctx->step_open = true;
         ctx->step_T = T;
@@ -526,6 +548,13 @@ int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t 
         *d_kv = ctx->kv;
     if (d_err)
         *d_err = ctx->err;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram fused decode: NULL context");
+    ctx->fused_decode = enable != 0;
     return ENGRAM_OK;
 }
 

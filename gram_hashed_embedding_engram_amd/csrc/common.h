@@ -30,6 +30,95 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Euclidean remainder a mod p for p > 0, in [0, p).
+__device__ __forceinline__ int64_t rem_euclid(int64_t a, int64_t p)
+{
+    const int64_t r = a % p;
+    return r < 0 ? r + p : r;
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// e4m3fn code -> f32, from the format: sign, 4 exponent bits (bias 7), 3
+// mantissa bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0)
+        return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
+    if (e == 15 && m == 7)
+        return __uint_as_float(0x7FC00000u | sign);
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// Values 8*sub .. 8*sub+7 (sub in 0..31) of one Q2_K block, given as its 21
+// dwords at b, as four packed bf16 pairs.  Block layout (GGML k-quant; the
+// pages give the size only): bytes 0..15 scale/min nibbles of the 16
+// sub-blocks of 16 values, bytes 16..79 the 2-bit quants, bytes 80..83 fp16
+// d and dmin.  Value e uses quant byte 32*(e/128) + e%32 at bit
+// 2*((e%128)/32) and sub-block e/16; for values 8*sub.. that is 8
+// consecutive quant bytes at 32*(sub/16) + 8*(sub%4), shift 2*((sub%16)/4),
+// sub-block sub/2.  y = d*scale*q - dmin*min: both products are exact in
+// f32, so the single subtraction and the bf16 rounding fix the result.
+template <class P>
+__device__ __forceinline__ u32x4 q2k_dequant8(P b, int sub)
+{
+    const uint32_t dd = b[20];
+    const float d = half_bits_to_f32(dd & 0xFFFFu);
+    const float dmin = half_bits_to_f32(dd >> 16);
+    const int sb = sub >> 1;
+    const uint32_t sc = (b[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
+    const float dl = d * (float)(sc & 15u);
+    const float ml = dmin * (float)(sc >> 4);
+    const int qw = 4 + 8 * (sub >> 4) + 2 * (sub & 3);      // dword of the 8 quants
+    const int shift = 2 * ((sub & 15) >> 2);
+    const uint32_t q0 = b[qw] >> shift, q1 = b[qw + 1] >> shift;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        y[k] = dl * (float)((q0 >> (8 * k)) & 3u) - ml;
+        y[4 + k] = dl * (float)((q1 >> (8 * k)) & 3u) - ml;
+    }
+    u32x4 o;
+    o.x = pack_bf16x2(y[0], y[1]);
+    o.y = pack_bf16x2(y[2], y[3]);
+    o.z = pack_bf16x2(y[4], y[5]);
+    o.w = pack_bf16x2(y[6], y[7]);
+    return o;
+}
+
+// Eight e4m3 codes (two dwords, first code in the low byte) times one
+// power-of-two scale, as four packed bf16 pairs (exact: e4m3 x 2^k fits bf16).
+__device__ __forceinline__ u32x4 e4m3_dequant8(uint32_t w0, uint32_t w1, float s)
+{
+    u32x4 o;
+    o.x = pack_bf16x2(e4m3_to_f32(w0 & 0xFFu) * s, e4m3_to_f32((w0 >> 8) & 0xFFu) * s);
+    o.y = pack_bf16x2(e4m3_to_f32((w0 >> 16) & 0xFFu) * s, e4m3_to_f32(w0 >> 24) * s);
+    o.z = pack_bf16x2(e4m3_to_f32(w1 & 0xFFu) * s, e4m3_to_f32((w1 >> 8) & 0xFFu) * s);
+    o.w = pack_bf16x2(e4m3_to_f32((w1 >> 16) & 0xFFu) * s, e4m3_to_f32(w1 >> 24) * s);
+    return o;
+}
+
+// acc + sum of the 8 products of two rows of 8 bf16 values (f32 fma chain).
+__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
+{
+    acc = fmaf(bf16_lo(w.x), bf16_lo(x.x), acc);
+    acc = fmaf(bf16_hi(w.x), bf16_hi(x.x), acc);
+    acc = fmaf(bf16_lo(w.y), bf16_lo(x.y), acc);
+    acc = fmaf(bf16_hi(w.y), bf16_hi(x.y), acc);
+    acc = fmaf(bf16_lo(w.z), bf16_lo(x.z), acc);
+    acc = fmaf(bf16_hi(w.z), bf16_hi(x.z), acc);
+    acc = fmaf(bf16_lo(w.w), bf16_lo(x.w), acc);
+    acc = fmaf(bf16_hi(w.w), bf16_hi(x.w), acc);
+    return acc;
+}
+
 // Sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v)
 {
@@ -91,6 +180,17 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
                           const Launch &l);
 int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
+
+// One decode token through hash, gather + dequant and the projection of one
+// layer in a single launch (decode.hip).  first_layer: the token's compressed
+// id comes from token_map[*ids] and is recorded in history[pos], and the row
+// ids of every layer are written to row_ids [n_layers][cols]; otherwise it is
+// read back from history[pos].  rows [cols*256] receives the dequantised rows.
+int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
+                      int64_t pos, int64_t *history, int32_t layer, bool first_layer,
+                      const engram_table &tab, const uint16_t *w, uint16_t *y, int64_t N,
+                      int64_t *row_ids, uint16_t *rows, int32_t *err, const Launch &l);
+constexpr int64_t kDecodeMaxCols = 32;     // cols*256 <= 8192 values in registers
 
 // GEMV covers T <= kGemvMaxT with K <= kGemvMaxK; larger T goes to the GEMM.
 constexpr int64_t kGemvMaxT = 4;

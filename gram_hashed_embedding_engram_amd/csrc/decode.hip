@@ -1,0 +1,207 @@
+// Decode step of one engram layer in one launch: hash of the token's n-gram
+// window (atlascybernetics "spark_model/layers/engram_v41.rs",
+// EngramHasher::hash), gather + dequant of its cols table rows
+// (rows_from_q2k; metrale "deepseek_v41_ref/engram.rs", regen_table and
+// embed_rows) and the wkv projection at one token (EngramV41::gemv_k;
+// linear_bf16).  The gate stays a separate launch.
+//
+// At one token the layer is one pass over wkv (252 MB at the decode shape);
+// hashing 24 ids and dequantising 24 rows is a few microseconds of latency.
+// Fused, that latency hides under the weight stream: every wavefront first
+// puts its first wkv row in flight, then its workgroup hashes the token (one
+// thread per (layer, column)), stages the needed 84-byte Q2_K blocks in LDS
+// with coalesced dword loads, expands them once per workgroup into the
+// token's bf16 activations (12 KiB of LDS), and each wavefront takes its
+// register slice of them.  The projection loop is the GEMV's: one wavefront
+// per output row at a time, K/512 non-temporal 1 KiB loads in flight, one
+// f32 wave sum, one bf16 rounding.  Workgroup 0 also writes the step's row
+// ids, the dequantised rows and the history entry, so the workspace holds
+// what the separate stages would have left there.
+#include "common.h"
+
+namespace engram {
+namespace {
+
+constexpr int kDecodeBlocksPerCu = 4;
+constexpr int kMaxChunks = kDecodeMaxCols * 32;   // 8-value chunks of the activations
+
+template <int FMT, int NI>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const HashConsts c, const int64_t *__restrict__ token_map, const int32_t *__restrict__ ids,
+    int64_t pos, int64_t *__restrict__ history, int layer, int first_layer,
+    const uint8_t *__restrict__ table, const float *__restrict__ scales, int64_t n_rows,
+    int scale_block, const uint16_t *__restrict__ w, uint16_t *__restrict__ y, int64_t N,
+    int64_t *__restrict__ row_ids, uint16_t *__restrict__ rows, int32_t *__restrict__ err)
+{
+    __shared__ int64_t s_id[kDecodeMaxCols];
+    __shared__ uint32_t s_blk[kDecodeMaxCols * 21];
+    __shared__ u32x4 s_x[kMaxChunks];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int cols = c.cols;
+    const int64_t K = (int64_t)cols * 256, kc = K >> 3;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // ---- the first wkv row of this wavefront goes out before anything else
+    u32x4 wv[NI];
+    {
+        const u32x4 *wr = (const u32x4 *)(w + min(wave, N - 1) * K);
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const int64_t idx = (int64_t)i * 64 + lane;
+            wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
+        }
+    }
+
+    // ---- hash: thread (l, col) computes layer l's id of column col; every
+    // workgroup needs its own layer's, workgroup 0 of the first layer writes all
+    if (tid < c.nl * cols) {
+        const int l = tid / cols, col = tid - l * cols;
+        if (l == layer || (blockIdx.x == 0 && first_layer)) {
+            int64_t own;
+            bool bad = false;
+            if (first_layer) {
+                const int32_t t = ids[0];
+                bad = t < 0 || (int64_t)t >= c.vocab;
+                own = bad ? -1 : token_map[t];       // reported, then hashed as unmapped
+            } else {
+                own = history[pos];
+            }
+            const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
+            bool blocked = own == -1;
+            const int64_t *m = c.mult + l * c.ng;
+            uint64_t r = (uint64_t)(blocked ? c.pad_id : own) * (uint64_t)m[0];
+#pragma unroll
+            for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
+                if (k < ngram) {
+                    const int64_t q = pos - k;
+                    const int64_t src = q >= 0 ? history[q] : 0;
+                    blocked = blocked || q < 0 || src == -1;
+                    r ^= (uint64_t)(blocked ? c.pad_id : src) * (uint64_t)m[k];
+                }
+            }
+            const int slot = l * cols + col;
+            const int64_t id = rem_euclid((int64_t)r, c.prime[slot]) + c.offset[slot];
+            if (blockIdx.x == 0) {
+                row_ids[slot] = id;
+                if (tid == 0 && first_layer) {
+                    history[pos] = own;
+                    if (bad && err)
+                        atomicOr(err, ENGRAM_DEVERR_TOKEN);
+                }
+            }
+            if (l == layer) {
+                const bool in_table = id >= 0 && id < n_rows;
+                if (!in_table && blockIdx.x == 0 && err)
+                    atomicOr(err, ENGRAM_DEVERR_ROW);
+                s_id[col] = in_table ? id : -1;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gather + dequant of the cols rows into the activations in LDS
+    if (FMT == ENGRAM_FMT_Q2K) {
+        for (int i = tid; i < cols * 21; i += 256) {
+            const int r = i / 21, d = i - r * 21;
+            const int64_t id = s_id[r];
+            s_blk[i] = id >= 0 ? *(const uint32_t *)(table + id * ENGRAM_Q2K_ROW_BYTES + 4 * d) : 0u;
+        }
+        __syncthreads();
+        for (int ch = tid; ch < kc; ch += 256) {
+            const int r = ch >> 5;
+            s_x[ch] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
+        }
+    } else {
+        const int nb = 256 / scale_block;
+        for (int ch = tid; ch < kc; ch += 256) {
+            const int r = ch >> 5, sub = ch & 31;
+            const int64_t id = s_id[r];
+            u32x4 o = zero;
+            if (id >= 0) {
+                const uint32_t *b = (const uint32_t *)(table + id * 256 + 8 * sub);
+                o = e4m3_dequant8(b[0], b[1], scales[id * nb + (8 * sub) / scale_block]);
+            }
+            s_x[ch] = o;
+        }
+    }
+    __syncthreads();
+    u32x4 xr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        const int64_t idx = (int64_t)i * 64 + lane;
+        xr[i] = idx < kc ? s_x[idx] : zero;
+    }
+    if (blockIdx.x == 0)
+        for (int ch = tid; ch < kc; ch += 256)
+            ((u32x4 *)rows)[ch] = s_x[ch];
+
+    // ---- projection: rows wave, wave + n_waves, ...
+    for (int64_t n = wave; n < N; n += n_waves) {
+        if (n != wave) {
+            const u32x4 *wr = (const u32x4 *)(w + n * K);
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+                const int64_t idx = (int64_t)i * 64 + lane;
+                wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
+            }
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            acc = dot8(wv[i], xr[i], acc);
+        const float s = wave_sum(acc);
+        if (lane == 0)
+            y[n] = f32_to_bf16(s);
+    }
+}
+
+}  // namespace
+
+int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
+                      int64_t pos, int64_t *history, int32_t layer, bool first_layer,
+                      const engram_table &tab, const uint16_t *w, uint16_t *y, int64_t N,
+                      int64_t *row_ids, uint16_t *rows, int32_t *err, const Launch &l)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    const int64_t K = (int64_t)c.cols * 256;
+    const int64_t ni = (K + 511) / 512;
+    int64_t blocks = (N + 3) / 4;
+    const int64_t cap = (int64_t)cus * kDecodeBlocksPerCu;
+    if (blocks > cap)
+        blocks = cap;
+    const dim3 grid((unsigned)blocks), block(256);
+#define ENGRAM_DECODE_CASE(NI_)                                                                  \
+    case NI_:                                                                                    \
+        if (tab.fmt == ENGRAM_FMT_Q2K)                                                           \
+            dispatch(decode_kernel<ENGRAM_FMT_Q2K, NI_>, grid, block, l, true, true, c, token_map, \
+                     ids, pos, history, (int)layer, (int)first_layer, tab.d_data, tab.d_scales,  \
+                     tab.n_rows, (int)tab.scale_block, w, y, N, row_ids, rows, err);             \
+        else                                                                                     \
+            dispatch(decode_kernel<ENGRAM_FMT_E4M3, NI_>, grid, block, l, true, true, c,         \
+                     token_map, ids, pos, history, (int)layer, (int)first_layer, tab.d_data,     \
+                     tab.d_scales, tab.n_rows, (int)tab.scale_block, w, y, N, row_ids, rows,     \
+                     err);                                                                       \
+        break;
+    switch (ni) {
+        ENGRAM_DECODE_CASE(1) ENGRAM_DECODE_CASE(2) ENGRAM_DECODE_CASE(3) ENGRAM_DECODE_CASE(4)
+        ENGRAM_DECODE_CASE(5) ENGRAM_DECODE_CASE(6) ENGRAM_DECODE_CASE(7) ENGRAM_DECODE_CASE(8)
+        ENGRAM_DECODE_CASE(9) ENGRAM_DECODE_CASE(10) ENGRAM_DECODE_CASE(11) ENGRAM_DECODE_CASE(12)
+        ENGRAM_DECODE_CASE(13) ENGRAM_DECODE_CASE(14) ENGRAM_DECODE_CASE(15) ENGRAM_DECODE_CASE(16)
+    default:
+        return fail(ENGRAM_E_UNSUPPORTED, "engram decode: %lld columns exceed %lld",
+                    (long long)c.cols, (long long)kDecodeMaxCols);
+    }
+#undef ENGRAM_DECODE_CASE
+    return launch_status("engram decode kernel");
+}
+
+}  // namespace engram

@@ -33,11 +33,6 @@ namespace {
 constexpr int kQ2kRows = 64;          // rows staged per workgroup iteration
 constexpr int kQ2kDwords = 21;        // 84 bytes
 
-__device__ __forceinline__ float half_bits_to_f32(uint32_t h)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
 __global__ __launch_bounds__(256) void gather_q2k_kernel(const uint8_t *__restrict__ table,
                                                          int64_t n_table_rows,
                                                          const int64_t *__restrict__ ids,
@@ -80,47 +75,13 @@ __global__ __launch_bounds__(256) void gather_q2k_kernel(const uint8_t *__restri
             const int64_t r = base + rr;
             if (r >= total_rows)
                 break;
-            const uint32_t *b = blk + rr * kQ2kDwords;
-            const uint32_t dd = b[20];
-            const float d = half_bits_to_f32(dd & 0xFFFFu);
-            const float dmin = half_bits_to_f32(dd >> 16);
-            const int sub = i >> 1;
-            const uint32_t sc = (b[sub >> 2] >> (8 * (sub & 3))) & 0xFFu;
-            const float dl = d * (float)(sc & 15u);
-            const float ml = dmin * (float)(sc >> 4);
-            const int qw = 4 + ((32 * (i >> 4) + 8 * (i & 3)) >> 2);   // dword of the 8 quants
-            const int shift = 2 * ((i & 15) >> 2);
-            const uint32_t q0 = b[qw] >> shift, q1 = b[qw + 1] >> shift;
-            float y[8];
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                y[k] = dl * (float)((q0 >> (8 * k)) & 3u) - ml;
-                y[4 + k] = dl * (float)((q1 >> (8 * k)) & 3u) - ml;
-            }
-            uint4 o;
-            o.x = pack_bf16x2(y[0], y[1]);
-            o.y = pack_bf16x2(y[2], y[3]);
-            o.z = pack_bf16x2(y[4], y[5]);
-            o.w = pack_bf16x2(y[6], y[7]);
+            u32x4 o = q2k_dequant8(blk + rr * kQ2kDwords, i);
             if (row_off[rr] < 0)
-                o = make_uint4(0, 0, 0, 0);
-            *(uint4 *)(out + r * 256 + 8 * i) = o;
+                o = u32x4{0u, 0u, 0u, 0u};
+            *(u32x4 *)(out + r * 256 + 8 * i) = o;
         }
         __syncthreads();
     }
-}
-
-// e4m3fn code -> f32, from the format: sign, 4 exponent bits (bias 7), 3
-// mantissa bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
-{
-    const uint32_t sign = (c & 0x80u) << 24;
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    if (e == 0)
-        return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
-    if (e == 15 && m == 7)
-        return __uint_as_float(0x7FC00000u | sign);
-    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
 }
 
 __global__ __launch_bounds__(256) void gather_e4m3_kernel(const uint8_t *__restrict__ codes,
@@ -145,19 +106,11 @@ __global__ __launch_bounds__(256) void gather_e4m3_kernel(const uint8_t *__restr
         const int64_t id = ids[t * id_stride + c];
         uint4 o0 = make_uint4(0, 0, 0, 0), o1 = o0;
         if (id >= 0 && id < n_table_rows) {
-            const uint4 v = *(const uint4 *)(codes + id * head_dim + 16 * ch);
+            const u32x4 v = *(const u32x4 *)(codes + id * head_dim + 16 * ch);
             const float s = scales[id * nb + (16 * ch) / scale_block];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t p[8];
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                p[2 * k] = pack_bf16x2(e4m3_to_f32(w[k] & 0xFFu) * s,
-                                       e4m3_to_f32((w[k] >> 8) & 0xFFu) * s);
-                p[2 * k + 1] = pack_bf16x2(e4m3_to_f32((w[k] >> 16) & 0xFFu) * s,
-                                           e4m3_to_f32(w[k] >> 24) * s);
-            }
-            o0 = make_uint4(p[0], p[1], p[2], p[3]);
-            o1 = make_uint4(p[4], p[5], p[6], p[7]);
+            const u32x4 p0 = e4m3_dequant8(v.x, v.y, s), p1 = e4m3_dequant8(v.z, v.w, s);
+            o0 = make_uint4(p0.x, p0.y, p0.z, p0.w);
+            o1 = make_uint4(p1.x, p1.y, p1.z, p1.w);
         } else if (err && ch == 0) {
             atomicOr(err, ENGRAM_DEVERR_ROW);
         }

@@ -19,20 +19,6 @@ namespace {
 
 constexpr int kGemvBlocksPerCu = 4;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
-{
-    acc = fmaf(bf16_lo(w.x), bf16_lo(x.x), acc);
-    acc = fmaf(bf16_hi(w.x), bf16_hi(x.x), acc);
-    acc = fmaf(bf16_lo(w.y), bf16_lo(x.y), acc);
-    acc = fmaf(bf16_hi(w.y), bf16_hi(x.y), acc);
-    acc = fmaf(bf16_lo(w.z), bf16_lo(x.z), acc);
-    acc = fmaf(bf16_hi(w.z), bf16_hi(x.z), acc);
-    acc = fmaf(bf16_lo(w.w), bf16_lo(x.w), acc);
-    acc = fmaf(bf16_hi(w.w), bf16_hi(x.w), acc);
-    return acc;
-}
 
 template <int NT, int NI>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ x,

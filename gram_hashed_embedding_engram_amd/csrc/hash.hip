@@ -17,12 +17,6 @@
 namespace engram {
 namespace {
 
-__device__ __forceinline__ int64_t rem_euclid(int64_t a, int64_t p)
-{
-    int64_t r = a % p;
-    return r < 0 ? r + p : r;
-}
-
 __global__ __launch_bounds__(256) void hash_kernel(const HashConsts c,
                                                    const int64_t *__restrict__ token_map,
                                                    const int32_t *__restrict__ ids, int64_t T,

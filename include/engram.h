@@ -253,9 +253,16 @@ int64_t engram_position(const engram_ctx *ctx);
 int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t **d_rows,
                            uint16_t **d_kv, int32_t **d_err);
 
+/* One decode token (T = 1, head_dim 256, at most 32 columns) runs hash,
+ * gather + dequant and the projection of a layer as one kernel, then the gate
+ * (enabled by default).  Results and workspace contents (row ids of every
+ * layer, rows, kv, history) are bit-identical to the staged path's.
+ * enable = 0 selects the staged kernels for every call. */
+int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable);
+
 /* Stage timing with HIP events recorded on the forward's stream, around each
  * kernel of every engram_forward while enabled (stages: 0 hash, 1 gather,
- * 2 projection, 3 gate).  engram_ctx_timing synchronises the events and
+ * 2 projection -- the fused decode kernel counts here --, 3 gate).  engram_ctx_timing synchronises the events and
  * returns, per stage, the summed milliseconds and the number of launches
  * since timing was enabled; it then clears them. */
 int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable);

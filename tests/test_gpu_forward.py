@@ -217,3 +217,67 @@ def test_forward_deterministic_and_device_error(E):
     assert ei.value.code == E.E_DEVICE
     ctx.reset()
     ctx.check()
+
+
+def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
+    """Prompt then single-token steps; returns per call (row ids, rows, kv, h)."""
+    out = []
+    d_ids = cuda(ids.astype(np.int32))
+    pos = 0
+    for step in range(1 + steps):
+        T = prompt if step == 0 else 1
+        h0 = h_prompt if step == 0 else h_steps[step - 1:step]
+        for layer in range(dev.w.n_layers):
+            d_h = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
+            ctx.forward(layer, d_ids[pos:pos + T] if layer == 0 else None, T, d_h)
+            rid, rows, kv = ctx.views(T)
+            out.append((rid.cpu().numpy(), to_np_u16(rows), to_np_u16(kv),
+                        d_h.cpu().numpy().view(np.uint32)))
+        pos += T
+    return out
+
+
+@pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name])
+def test_fused_decode_matches_staged(E, name):
+    """The one-launch decode layer (hash + gather + projection) leaves exactly
+    what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""
+    dev = Device(name)
+    w = dev.w
+    log(f"fused vs staged decode: {name}")
+    prompt, steps = 8, 24
+    ids = G.token_ids(w, prompt + steps)
+    hp = G.highway(w, prompt)
+    hs = G.highway(w, steps, decode=True) if w.decode_steps else G.highway(w, steps)
+    res = []
+    for fused in (True, False):
+        ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps)
+        ctx.set_fused_decode(fused)
+        res.append(run_steps(dev, ctx, ids, steps, prompt, hp, hs))
+        ctx.check()
+    for i, (a, b) in enumerate(zip(*res)):
+        for x, y, what in zip(a, b, ("row ids", "rows", "kv", "highway")):
+            np.testing.assert_array_equal(x, y, err_msg=f"call {i}: {what}")
+    # and the hash of the steps equals the oracle's single pass
+    want = dev.oracle_hasher(prompt + steps).hash(ids, 0)
+    calls = res[0][::w.n_layers]
+    np.testing.assert_array_equal(calls[-1][0], want[-1:])
+
+
+def test_fused_decode_bad_token(E):
+    w = synth.TINY_E4M3
+    dev = Device(w.name)
+    ids = G.token_ids(w, 12).copy()
+    unmapped = int(np.nonzero(dev.ht["token_map"] == -1)[0][0])
+    bad = ids.copy()
+    bad[9] = w.vocab + 7
+    subst = ids.copy()
+    subst[9] = unmapped
+    ctx = dev.context(max_tokens=8, max_seq=12)
+    hp, hs = G.highway(w, 8), G.highway(w, 4)
+    out = run_steps(dev, ctx, bad, 4, 8, hp, hs)
+    with pytest.raises(E.EngramError) as ei:
+        ctx.check()
+    assert ei.value.code == E.E_DEVICE
+    want = dev.oracle_hasher(12).hash(subst, 0)
+    for step in range(1, 5):
+        np.testing.assert_array_equal(out[step][0], want[7 + step:8 + step])
