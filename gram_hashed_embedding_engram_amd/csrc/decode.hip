@@ -11,8 +11,9 @@
 // puts its first wkv row in flight, then its workgroup hashes the token (one
 // thread per (layer, column)), stages the needed 84-byte Q2_K blocks in LDS
 // with coalesced dword loads, expands them once per workgroup into the
-// token's bf16 activations (12 KiB of LDS), and each wavefront takes its
-// register slice of them.  The projection loop is the GEMV's: one wavefront
+// token's bf16 activations (12 KiB of LDS), which the wavefronts read back
+// per row (registers hold only the weight row in flight, so four workgroups
+// stay resident per CU).  The projection loop is the GEMV's: one wavefront
 // per output row at a time, K/512 non-temporal 1 KiB loads in flight, one
 // f32 wave sum, one bf16 rounding.  Workgroup 0 also writes the step's row
 // ids, the dequantised rows and the history entry, so the workspace holds
@@ -127,12 +128,6 @@ __global__ __launch_bounds__(256) void decode_kernel(
         }
     }
     __syncthreads();
-    u32x4 xr[NI];
-#pragma unroll
-    for (int i = 0; i < NI; i++) {
-        const int64_t idx = (int64_t)i * 64 + lane;
-        xr[i] = idx < kc ? s_x[idx] : zero;
-    }
     if (blockIdx.x == 0)
         for (int ch = tid; ch < kc; ch += 256)
             ((u32x4 *)rows)[ch] = s_x[ch];
@@ -147,10 +142,14 @@ __global__ __launch_bounds__(256) void decode_kernel(
                 wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
             }
         }
+        // the activations stay in LDS (16-byte reads, consecutive lanes):
+        // registers hold only the weight row in flight
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NI; i++)
-            acc = dot8(wv[i], xr[i], acc);
+        for (int i = 0; i < NI; i++) {
+            const int64_t idx = (int64_t)i * 64 + lane;
+            acc = dot8(wv[i], idx < kc ? s_x[idx] : zero, acc);
+        }
         const float s = wave_sum(acc);
         if (lane == 0)
             y[n] = f32_to_bf16(s);
