@@ -156,6 +156,8 @@ int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t 
     CHECK(dim >= 256 && dim % 256 == 0 && dim <= (1 << 20), ENGRAM_E_UNSUPPORTED,
           "engram gate: dim = %lld must be a multiple of 256", (long long)dim);
     CHECK(std::isfinite(eps) && eps >= 0.0f, ENGRAM_E_ARG, "engram gate: eps = %g", (double)eps);
+    CHECK(T < ((int64_t)1 << 24) / hc, ENGRAM_E_RANGE, "engram gate: %lld x %d rows exceed 2^24",
+          (long long)T, hc);
     if (T == 0)
         return ENGRAM_OK;
     CHECK(h && kv && qk, ENGRAM_E_ARG, "engram gate: NULL pointer");
@@ -196,6 +198,7 @@ struct engram_ctx {
     int64_t step_T = 0;
     int64_t step_start = 0;
     bool fused_decode = true;
+    bool was_reset = false;
     bool timing = false;
     std::vector<TimingRec> recs;
     std::vector<hipEvent_t> pool;
@@ -441,6 +444,7 @@ int32_t engram_reset(engram_ctx *ctx, void *stream)
     ctx->pos = 0;
     ctx->step_open = false;
     ctx->step_T = 0;
+    ctx->was_reset = true;
     return ENGRAM_OK;
 }
 
@@ -468,6 +472,7 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
               "engram forward: layer %d got %lld tokens, the step has %lld", hash_index,
               (long long)T, (long long)ctx->step_T);
     }
+    CHECK(ctx->was_reset, ENGRAM_E_STATE, "engram forward: the context needs engram_reset first");
     hipStream_t s = as_stream(stream);
     const engram_config &cfg = ctx->cfg;
     int32_t rc;

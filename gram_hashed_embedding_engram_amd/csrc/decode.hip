@@ -3,7 +3,7 @@
 // EngramHasher::hash), gather + dequant of its cols table rows
 // (rows_from_q2k; metrale "deepseek_v41_ref/engram.rs", regen_table and
 // embed_rows) and the wkv projection at one token (EngramV41::gemv_k;
-// linear_bf16).  The gate stays a separate launch.
+// linear_bf16).
 //
 // At one token the layer is one pass over wkv (252 MB at the decode shape);
 // hashing 24 ids and dequantising 24 rows is a few microseconds of latency.
@@ -15,9 +15,16 @@
 // per row (registers hold only the weight row in flight, so four workgroups
 // stay resident per CU).  The projection loop is the GEMV's: one wavefront
 // per output row at a time, K/512 non-temporal 1 KiB loads in flight, one
-// f32 wave sum, one bf16 rounding.  Workgroup 0 also writes the step's row
-// ids, the dequantised rows and the history entry, so the workspace holds
-// what the separate stages would have left there.
+// f32 wave sum, one bf16 rounding, the store issued after the next row's
+// loads.  Workgroup 0 also writes the step's row ids, the dequantised rows
+// and the history entry, so the workspace holds what the separate stages
+// would have left there.
+//
+// The gate stays a launch of its own.  It needs every kv row, and doing it
+// in the last workgroup to finish was measured slower: the completion count
+// and the device-wide visibility of kv cost about 4 us per launch, and four
+// gate rows on one compute unit take twice as long as the gate kernel's
+// four workgroups.
 #include "common.h"
 
 namespace engram {
@@ -132,7 +139,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
         for (int ch = tid; ch < kc; ch += 256)
             ((u32x4 *)rows)[ch] = s_x[ch];
 
-    // ---- projection: rows wave, wave + n_waves, ...
+    // ---- projection: rows wave, wave + n_waves, ...  A row's result is
+    // stored after the next row's loads are issued, so the loop's wait for
+    // those loads does not also wait for the store.
+    int64_t prev_n = -1;
+    uint16_t prev_v = 0;
     for (int64_t n = wave; n < N; n += n_waves) {
         if (n != wave) {
             const u32x4 *wr = (const u32x4 *)(w + n * K);
@@ -142,6 +153,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
                 wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
             }
         }
+        if (lane == 0 && prev_n >= 0)
+            y[prev_n] = prev_v;
         // the activations stay in LDS (16-byte reads, consecutive lanes):
         // registers hold only the weight row in flight
         float acc = 0.0f;
@@ -150,10 +163,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
             const int64_t idx = (int64_t)i * 64 + lane;
             acc = dot8(wv[i], idx < kc ? s_x[idx] : zero, acc);
         }
-        const float s = wave_sum(acc);
-        if (lane == 0)
-            y[n] = f32_to_bf16(s);
+        prev_v = f32_to_bf16(wave_sum(acc));
+        prev_n = n;
     }
+    if (lane == 0 && prev_n >= 0)
+        y[prev_n] = prev_v;
 }
 
 }  // namespace

@@ -3,126 +3,49 @@
 // "spark_model/layers/engram_v41.rs", module doc stage 4 and
 // EngramV41::upload_qk).
 //
-// One wavefront per (token, stream).  A lane holds 4 consecutive highway
-// values of each 256-wide chunk in registers (dim/64 values), so h is read
-// once and written once; the three sums (h.h, key.key, h.qk.key) are f32
-// partials reduced across the wave, the scalar gate is computed by every
-// lane, and h += gate * value is written back with 16-byte stores.  The
-// value row is shared by the hc streams of a token and is read from L2 after
-// the first wave.  Widths above 4096 take a two-pass variant that re-reads h.
+// One workgroup of four wavefronts per (token, stream) row: wavefront w
+// takes the 256-wide chunks w, w+4, ... of the row, with every load of h,
+// qk, the key and the value in flight at once and h held in registers from
+// the sums to the update, so h is read once and written once.  The three
+// sums (h.h, key.key, h.qk.key) are f32, reduced per lane, per wavefront,
+// then over the four wavefronts in a fixed order, so the result does not
+// depend on T or on the kernel variant.  A single token's hc rows thus
+// spread over hc compute units instead of queueing on one.
 #include "common.h"
 
 namespace engram {
 namespace {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kGateMaxI = 8;   // chunks per wavefront held in registers: dim <= 8192
 
-__device__ __forceinline__ float gate_value(float hh, float kk, float dot, float fdim,
-                                            float inv_sqrt_dim, float eps)
-{
-    const float rstd = (1.0f / sqrtf(hh / fdim + eps)) * (1.0f / sqrtf(kk / fdim + eps));
-    const float s = dot * rstd * inv_sqrt_dim;
-    const float g = copysignf(sqrtf(fmaxf(fabsf(s), 1e-6f)), s);
-    return 1.0f / (1.0f + expf(-g));
-}
-
-template <int NCH>
+template <int MAXI>
 __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
                                                    const uint16_t *__restrict__ kv,
-                                                   const float *__restrict__ qk, int64_t T, int hc,
+                                                   const float *__restrict__ qk, int hc,
                                                    int64_t dim, float eps, float fdim,
                                                    float inv_sqrt_dim)
 {
-    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int lane = threadIdx.x & 63;
-    if (wid >= T * hc)
-        return;
-    const int64_t t = wid / hc;
-    const int c = (int)(wid - t * hc);
-    float *hp = h + wid * dim;
-    const uint16_t *key = kv + t * (hc + 1) * dim + (int64_t)c * dim;
-    const uint16_t *val = kv + t * (hc + 1) * dim + (int64_t)hc * dim;
-    const float *q = qk + (int64_t)c * dim;
-
-    float4 hv[NCH];
-    float hh = 0.0f, kk = 0.0f, dot = 0.0f;
-#pragma unroll
-    for (int ch = 0; ch < NCH; ch++) {
-        const int64_t idx = (int64_t)ch * 256 + lane * 4;
-        hv[ch] = *(const float4 *)(hp + idx);
-        const u32x2 k2 = *(const u32x2 *)(key + idx);
-        const float4 q4 = *(const float4 *)(q + idx);
-        const float kf[4] = {bf16_lo(k2.x), bf16_hi(k2.x), bf16_lo(k2.y), bf16_hi(k2.y)};
-        const float hf[4] = {hv[ch].x, hv[ch].y, hv[ch].z, hv[ch].w};
-        const float qf[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            hh += hf[e] * hf[e];
-            kk += kf[e] * kf[e];
-            dot += hf[e] * qf[e] * kf[e];
-        }
-    }
-    hh = wave_sum(hh);
-    kk = wave_sum(kk);
-    dot = wave_sum(dot);
-    const float gate = gate_value(hh, kk, dot, fdim, inv_sqrt_dim, eps);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ch++) {
-        const int64_t idx = (int64_t)ch * 256 + lane * 4;
-        const u32x2 v2 = *(const u32x2 *)(val + idx);
-        float4 o = hv[ch];
-        o.x += gate * bf16_lo(v2.x);
-        o.y += gate * bf16_hi(v2.x);
-        o.z += gate * bf16_lo(v2.y);
-        o.w += gate * bf16_hi(v2.y);
-        *(float4 *)(hp + idx) = o;
-    }
+    const int64_t row = blockIdx.x;
+    const int64_t t = row / hc;
+    const int c = (int)(row - t * hc);
+    const uint16_t *kvt = kv + t * (hc + 1) * dim;
+    gate_row<MAXI>(h + row * dim, kvt + (int64_t)c * dim, qk + (int64_t)c * dim,
+                   kvt + (int64_t)hc * dim, (int)(dim >> 8), eps, fdim, inv_sqrt_dim);
 }
 
-// Any multiple of 256: first pass sums, second pass re-reads h and updates.
-__global__ __launch_bounds__(256) void gate_kernel_2pass(float *__restrict__ h,
-                                                         const uint16_t *__restrict__ kv,
-                                                         const float *__restrict__ qk, int64_t T,
-                                                         int hc, int64_t dim, float eps,
-                                                         float fdim, float inv_sqrt_dim)
+// Any multiple of 256 (h is read again for the update).
+__global__ __launch_bounds__(256) void gate_kernel_any(float *__restrict__ h,
+                                                       const uint16_t *__restrict__ kv,
+                                                       const float *__restrict__ qk, int hc,
+                                                       int64_t dim, float eps, float fdim,
+                                                       float inv_sqrt_dim)
 {
-    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int lane = threadIdx.x & 63;
-    if (wid >= T * hc)
-        return;
-    const int64_t t = wid / hc;
-    const int c = (int)(wid - t * hc);
-    float *hp = h + wid * dim;
-    const uint16_t *key = kv + t * (hc + 1) * dim + (int64_t)c * dim;
-    const uint16_t *val = kv + t * (hc + 1) * dim + (int64_t)hc * dim;
-    const float *q = qk + (int64_t)c * dim;
-    float hh = 0.0f, kk = 0.0f, dot = 0.0f;
-    for (int64_t idx = lane * 4; idx < dim; idx += 256) {
-        const float4 hv = *(const float4 *)(hp + idx);
-        const u32x2 k2 = *(const u32x2 *)(key + idx);
-        const float4 q4 = *(const float4 *)(q + idx);
-        const float kf[4] = {bf16_lo(k2.x), bf16_hi(k2.x), bf16_lo(k2.y), bf16_hi(k2.y)};
-        const float hf[4] = {hv.x, hv.y, hv.z, hv.w};
-        const float qf[4] = {q4.x, q4.y, q4.z, q4.w};
-        for (int e = 0; e < 4; e++) {
-            hh += hf[e] * hf[e];
-            kk += kf[e] * kf[e];
-            dot += hf[e] * qf[e] * kf[e];
-        }
-    }
-    hh = wave_sum(hh);
-    kk = wave_sum(kk);
-    dot = wave_sum(dot);
-    const float gate = gate_value(hh, kk, dot, fdim, inv_sqrt_dim, eps);
-    for (int64_t idx = lane * 4; idx < dim; idx += 256) {
-        const u32x2 v2 = *(const u32x2 *)(val + idx);
-        float4 o = *(const float4 *)(hp + idx);
-        o.x += gate * bf16_lo(v2.x);
-        o.y += gate * bf16_hi(v2.x);
-        o.z += gate * bf16_lo(v2.y);
-        o.w += gate * bf16_hi(v2.y);
-        *(float4 *)(hp + idx) = o;
-    }
+    const int64_t row = blockIdx.x;
+    const int64_t t = row / hc;
+    const int c = (int)(row - t * hc);
+    const uint16_t *kvt = kv + t * (hc + 1) * dim;
+    gate_row_any(h + row * dim, kvt + (int64_t)c * dim, qk + (int64_t)c * dim,
+                 kvt + (int64_t)hc * dim, (int)(dim >> 8), eps, fdim, inv_sqrt_dim);
 }
 
 __global__ __launch_bounds__(256) void qk_kernel(const uint16_t *__restrict__ q,
@@ -146,31 +69,28 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
                     int64_t dim, float eps, const Launch &l)
 {
-    const int64_t waves = T * hc;
-    if (waves == 0)
+    const int64_t rows = T * hc;
+    if (rows == 0)
         return ENGRAM_OK;
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const dim3 grid((unsigned)rows), block(256);
     const float fdim = (float)dim;
     const float inv_sqrt_dim = powf(fdim, -0.5f);
-    const int64_t nch = dim / 256;
-    const bool in_registers = nch == 1 || nch == 2 || nch == 4 || nch == 8 || nch == 16;
-#define ENGRAM_GATE_CASE(N_)                                                              \
-    case N_:                                                                              \
-        dispatch(gate_kernel<N_>, grid, block, l, true, true, h, kv, qk, T, hc, dim, eps, fdim, \
-                 inv_sqrt_dim);                                                          \
+    const int64_t maxi = (dim / 256 + 3) / 4;
+#define ENGRAM_GATE_CASE(I_)                                                                   \
+    case I_:                                                                                   \
+        dispatch(gate_kernel<I_>, grid, block, l, true, true, h, kv, qk, (int)hc, dim, eps,    \
+                 fdim, inv_sqrt_dim);                                                         \
         break;
-    if (in_registers) {
-        switch (nch) {
-            ENGRAM_GATE_CASE(1) ENGRAM_GATE_CASE(2) ENGRAM_GATE_CASE(4) ENGRAM_GATE_CASE(8)
-            ENGRAM_GATE_CASE(16)
-        default:
-            break;
-        }
-    } else {
-        dispatch(gate_kernel_2pass, grid, block, l, true, true, h, kv, qk, T, hc, dim, eps, fdim,
+    switch (maxi) {
+        ENGRAM_GATE_CASE(1) ENGRAM_GATE_CASE(2) ENGRAM_GATE_CASE(3) ENGRAM_GATE_CASE(4)
+        ENGRAM_GATE_CASE(5) ENGRAM_GATE_CASE(6) ENGRAM_GATE_CASE(7) ENGRAM_GATE_CASE(8)
+    default:
+        dispatch(gate_kernel_any, grid, block, l, true, true, h, kv, qk, (int)hc, dim, eps, fdim,
                  inv_sqrt_dim);
+        break;
     }
 #undef ENGRAM_GATE_CASE
+    static_assert(kGateMaxI == 8, "dispatch covers 1..kGateMaxI");
     return launch_status("engram gate kernel");
 }
 

@@ -235,8 +235,10 @@ int32_t engram_reset(engram_ctx *ctx, void *stream);
  * "deepseek_v41_layer.rs", V41Runtime::step_hashes: computed by the first
  * engram layer, reused by the second).
  * Refuses T > max_tokens or position + T > max_seq (ENGRAM_E_RANGE),
- * an unregistered layer or a call with no open step / another T
- * (ENGRAM_E_STATE). */
+ * an unregistered layer, a call with no open step / another T, or a context
+ * that has not been through engram_reset (ENGRAM_E_STATE).  Calls on one
+ * context must not overlap (one stream, or ordered streams): they share its
+ * workspace. */
 int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids, int64_t T,
                        float *d_h, void *stream);
 
@@ -256,13 +258,13 @@ int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t 
 /* One decode token (T = 1, head_dim 256, at most 32 columns) runs hash,
  * gather + dequant and the projection of a layer as one kernel, then the gate
  * (enabled by default).  Results and workspace contents (row ids of every
- * layer, rows, kv, history) are bit-identical to the staged path's.
+ * layer, rows, kv, history, highway) are bit-identical to the staged path's.
  * enable = 0 selects the staged kernels for every call. */
 int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable);
 
 /* Stage timing with HIP events recorded on the forward's stream, around each
  * kernel of every engram_forward while enabled (stages: 0 hash, 1 gather,
- * 2 projection -- the fused decode kernel counts here --, 3 gate).  engram_ctx_timing synchronises the events and
+ * 2 projection -- the one-launch decode kernel counts here --, 3 gate).  engram_ctx_timing synchronises the events and
  * returns, per stage, the summed milliseconds and the number of launches
  * since timing was enabled; it then clears them. */
 int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable);

@@ -193,6 +193,9 @@ def test_context_refusals_and_state(L):
         assert L.engram_forward(h, 0, None, 1, FAKE, None) == E.E_ARG
         assert L.engram_forward(h, 0, FAKE, 1, FAKE + 4, None) == E.E_ARG
         assert L.engram_forward(h, 3, FAKE, 1, FAKE, None) == E.E_ARG
+        # a valid call before the first engram_reset (nothing is launched)
+        rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 1, FAKE, None))
+        assert rc == E.E_STATE and "engram_reset" in msg
         # timing with nothing recorded makes no runtime call
         assert L.engram_ctx_set_timing(h, 1) == E.OK
         ms = (ctypes.c_double * 4)()

@@ -264,7 +264,8 @@ def test_qk_product_exact(E, decode):
 
 
 @pytest.mark.parametrize("T,hc,dim", [(64, 4, 256), (1, 4, 4096), (37, 3, 4096), (5, 2, 768),
-                                      (3, 1, 4352), (9, 4, 1024), (4096, 4, 4096)])
+                                      (3, 1, 4352), (9, 4, 1024), (4096, 4, 4096), (2, 2, 8192),
+                                      (3, 2, 9216)])
 def test_gate(E, T, hc, dim):
     import oracle
     rng = np.random.default_rng(T * 7 + dim)
@@ -292,3 +293,21 @@ def test_gate(E, T, hc, dim):
     d_h = torch.from_numpy(h).cuda()
     E.gate_apply(d_h, cuda(kv0.reshape(T, -1)), d_qk, 1e-6)
     np.testing.assert_array_equal(d_h.cpu().numpy().view(np.uint32), h.view(np.uint32))
+
+
+@pytest.mark.parametrize("dim", [4096, 9216])
+def test_gate_rows_independent_of_T(E, dim):
+    """A token's gated rows are the same bits whether it is gated alone
+    (decode) or inside a batch (prefill): the reduction order is per row."""
+    rng = np.random.default_rng(dim)
+    T, hc = 6, 4
+    h = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = bf16_rand(rng, (T, dim * (hc + 1)), 0.5)
+    d_qk = torch.from_numpy(rng.standard_normal((hc, dim)).astype(np.float32) * 0.05).cuda()
+    d_all = torch.from_numpy(h).cuda()
+    E.gate_apply(d_all, cuda(kv), d_qk, 1e-6)
+    for t in (0, 5):
+        d_one = torch.from_numpy(h[t:t + 1].copy()).cuda()
+        E.gate_apply(d_one, cuda(kv[t:t + 1].copy()), d_qk, 1e-6)
+        np.testing.assert_array_equal(d_one.cpu().numpy().view(np.uint32),
+                                      d_all[t:t + 1].cpu().numpy().view(np.uint32))
