@@ -49,8 +49,13 @@ def log(*a):
 
 
 def source_digest(name):
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of a kernel source followed by the
+    shared header it includes."""
+    h = hashlib.sha256()
+    for f in (name, "common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(summary, kernel_src):

@@ -16,16 +16,173 @@
 namespace engram {
 namespace {
 
+// The gate of one (token, stream) row by one wavefront (metrale
+// "deepseek_v41_ref/engram.rs", gate_and_add): the sigmoid of the signed
+// square root of the scaled, doubly normalised h.qk.key product.
+__device__ __forceinline__ float gate_value(float hh, float kk, float dot, float fdim,
+                                            float inv_sqrt_dim, float eps)
+{
+    const float rstd = (1.0f / sqrtf(hh / fdim + eps)) * (1.0f / sqrtf(kk / fdim + eps));
+    const float s = dot * rstd * inv_sqrt_dim;
+    const float g = copysignf(sqrtf(fmaxf(fabsf(s), 1e-6f)), s);
+    return 1.0f / (1.0f + expf(-g));
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One 4-value piece of a gate row: the three f32 sums h.h, key.key and
+// h.qk.key, each an explicit fma chain so every kernel that calls this
+// rounds the same way.
+__device__ __forceinline__ void gate_accum(const float4 &h, const float4 &q, const u32x2 &k,
+                                           float &hh, float &kk, float &dot)
+{
+    const float kf[4] = {bf16_lo(k.x), bf16_hi(k.x), bf16_lo(k.y), bf16_hi(k.y)};
+    const float hf[4] = {h.x, h.y, h.z, h.w};
+    const float qf[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        hh = fmaf(hf[e], hf[e], hh);
+        kk = fmaf(kf[e], kf[e], kk);
+        dot = fmaf(hf[e] * qf[e], kf[e], dot);
+    }
+}
+
+__device__ __forceinline__ float4 gate_update(float4 h, float gate, const u32x2 &v)
+{
+    h.x = fmaf(gate, bf16_lo(v.x), h.x);
+    h.y = fmaf(gate, bf16_hi(v.x), h.y);
+    h.z = fmaf(gate, bf16_lo(v.y), h.z);
+    h.w = fmaf(gate, bf16_hi(v.y), h.w);
+    return h;
+}
+
+// The gate of one (token, stream) row by the four wavefronts of a workgroup
+// (every thread of the workgroup calls it).  The row is dim = 256*nch
+// values; wavefront w takes its chunks w, w+4, w+8, ... (at most MAXI of
+// them) and lane l values 4l..4l+3 of each.  Every load (h, qk, key, value)
+// is issued before any arithmetic and h stays in registers from the sums to
+// the update.  Each lane sums its chunks in order, the wavefront reduces its
+// lanes, and the four wavefront partials are added in order through LDS;
+// that sequence does not depend on MAXI.
+template <int MAXI>
+__device__ __forceinline__ void gate_row(float *__restrict__ hp, const uint16_t *__restrict__ key,
+                                         const float *__restrict__ q,
+                                         const uint16_t *__restrict__ val, int nch, float eps,
+                                         float fdim, float inv_sqrt_dim)
+{
+    __shared__ float s_part[4][3];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float4 hv[MAXI], qv[MAXI];
+    u32x2 kv[MAXI], vv[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; i++) {
+        const int idx = (w + 4 * i) * 256 + lane * 4;
+        if (w + 4 * i < nch) {
+            hv[i] = *(const float4 *)(hp + idx);
+            qv[i] = *(const float4 *)(q + idx);
+            kv[i] = *(const u32x2 *)(key + idx);
+            vv[i] = *(const u32x2 *)(val + idx);
+        }
+    }
+    float hh = 0.0f, kk = 0.0f, dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXI; i++)
+        if (w + 4 * i < nch)
+            gate_accum(hv[i], qv[i], kv[i], hh, kk, dot);
+    hh = wave_sum(hh);
+    kk = wave_sum(kk);
+    dot = wave_sum(dot);
+    if (lane == 0) {
+        s_part[w][0] = hh;
+        s_part[w][1] = kk;
+        s_part[w][2] = dot;
+    }
+    __syncthreads();
+    float t[3];
+#pragma unroll
+    for (int j = 0; j < 3; j++)
+        t[j] = ((s_part[0][j] + s_part[1][j]) + s_part[2][j]) + s_part[3][j];
+    const float gate = gate_value(t[0], t[1], t[2], fdim, inv_sqrt_dim, eps);
+#pragma unroll
+    for (int i = 0; i < MAXI; i++)
+        if (w + 4 * i < nch)
+            *(float4 *)(hp + (w + 4 * i) * 256 + lane * 4) = gate_update(hv[i], gate, vv[i]);
+}
+
+// The same row, with the same bits, for any nch: the chunks are taken in
+// batches of 4 (h read again for the update).
+__device__ __forceinline__ void gate_row_any(float *__restrict__ hp,
+                                             const uint16_t *__restrict__ key,
+                                             const float *__restrict__ q,
+                                             const uint16_t *__restrict__ val, int nch, float eps,
+                                             float fdim, float inv_sqrt_dim)
+{
+    __shared__ float s_part[4][3];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float hh = 0.0f, kk = 0.0f, dot = 0.0f;
+    for (int i0 = 0; w + 4 * i0 < nch; i0 += 4) {
+        float4 hv[4], qv[4];
+        u32x2 kv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ch = w + 4 * (i0 + i);
+            if (ch < nch) {
+                hv[i] = *(const float4 *)(hp + ch * 256 + lane * 4);
+                qv[i] = *(const float4 *)(q + ch * 256 + lane * 4);
+                kv[i] = *(const u32x2 *)(key + ch * 256 + lane * 4);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (w + 4 * (i0 + i) < nch)
+                gate_accum(hv[i], qv[i], kv[i], hh, kk, dot);
+    }
+    hh = wave_sum(hh);
+    kk = wave_sum(kk);
+    dot = wave_sum(dot);
+    if (lane == 0) {
+        s_part[w][0] = hh;
+        s_part[w][1] = kk;
+        s_part[w][2] = dot;
+    }
+    __syncthreads();
+    float t[3];
+#pragma unroll
+    for (int j = 0; j < 3; j++)
+        t[j] = ((s_part[0][j] + s_part[1][j]) + s_part[2][j]) + s_part[3][j];
+    const float gate = gate_value(t[0], t[1], t[2], fdim, inv_sqrt_dim, eps);
+    for (int ch = w; ch < nch; ch += 4) {
+        float *p = hp + ch * 256 + lane * 4;
+        *(float4 *)p = gate_update(*(const float4 *)p, gate, *(const u32x2 *)(val + ch * 256 + lane * 4));
+    }
+}
+
 constexpr int kGateMaxI = 8;   // chunks per wavefront held in registers: dim <= 8192
+
+// Workgroup b -> row (token * hc + stream).  Workgroups are dispatched to
+// the eight XCDs in turn, so b, b+8, b+16, ... share an L2: the hc rows of
+// a token go to hc such workgroups, and the token's value row (and key
+// rows' lines) are fetched from HBM once instead of once per stream.  The
+// last T % 8 tokens keep the plain order.
+__device__ __forceinline__ int64_t token_row(int64_t b, int64_t T, int hc)
+{
+    const int64_t grouped = (T & ~(int64_t)7) * hc;
+    if (b >= grouped)
+        return b;
+    const int64_t s = b >> 3;
+    const int64_t k = s / hc;
+    const int c = (int)(s - k * hc);
+    return ((k << 3) + (b & 7)) * hc + c;
+}
 
 template <int MAXI>
 __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
                                                    const uint16_t *__restrict__ kv,
-                                                   const float *__restrict__ qk, int hc,
-                                                   int64_t dim, float eps, float fdim,
+                                                   const float *__restrict__ qk, int64_t T,
+                                                   int hc, int64_t dim, float eps, float fdim,
                                                    float inv_sqrt_dim)
 {
-    const int64_t row = blockIdx.x;
+    const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
     const int c = (int)(row - t * hc);
     const uint16_t *kvt = kv + t * (hc + 1) * dim;
@@ -36,11 +193,11 @@ __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
 // Any multiple of 256 (h is read again for the update).
 __global__ __launch_bounds__(256) void gate_kernel_any(float *__restrict__ h,
                                                        const uint16_t *__restrict__ kv,
-                                                       const float *__restrict__ qk, int hc,
-                                                       int64_t dim, float eps, float fdim,
-                                                       float inv_sqrt_dim)
+                                                       const float *__restrict__ qk, int64_t T,
+                                                       int hc, int64_t dim, float eps,
+                                                       float fdim, float inv_sqrt_dim)
 {
-    const int64_t row = blockIdx.x;
+    const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
     const int c = (int)(row - t * hc);
     const uint16_t *kvt = kv + t * (hc + 1) * dim;
@@ -78,15 +235,15 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
     const int64_t maxi = (dim / 256 + 3) / 4;
 #define ENGRAM_GATE_CASE(I_)                                                                   \
     case I_:                                                                                   \
-        dispatch(gate_kernel<I_>, grid, block, l, true, true, h, kv, qk, (int)hc, dim, eps,    \
+        dispatch(gate_kernel<I_>, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps, \
                  fdim, inv_sqrt_dim);                                                         \
         break;
     switch (maxi) {
         ENGRAM_GATE_CASE(1) ENGRAM_GATE_CASE(2) ENGRAM_GATE_CASE(3) ENGRAM_GATE_CASE(4)
         ENGRAM_GATE_CASE(5) ENGRAM_GATE_CASE(6) ENGRAM_GATE_CASE(7) ENGRAM_GATE_CASE(8)
     default:
-        dispatch(gate_kernel_any, grid, block, l, true, true, h, kv, qk, (int)hc, dim, eps, fdim,
-                 inv_sqrt_dim);
+        dispatch(gate_kernel_any, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps,
+                 fdim, inv_sqrt_dim);
         break;
     }
 #undef ENGRAM_GATE_CASE
