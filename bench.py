@@ -50,11 +50,15 @@ def log(*a):
 
 def source_digest(name):
     """First 16 hex digits of the SHA-256 of a kernel source followed by the
-    shared header it includes."""
+    shared header it includes, with // comments and blank lines removed (a
+    comment edit does not change the kernel)."""
     h = hashlib.sha256()
     for f in (name, "common.h"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

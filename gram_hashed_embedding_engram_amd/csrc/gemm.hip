@@ -8,19 +8,20 @@
 // K-contiguous.
 //
 // Tiling: a 256-thread workgroup (4 wavefronts, one per SIMD) owns a 256x256
-// output tile and walks K in steps of 64.  Each wavefront owns a 128x128
+// output tile and walks K in tiles of 32.  Each wavefront owns a 128x128
 // quarter as 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 f32 accumulators a
 // lane).  The matrix-core "A" operand is fed from wkv and the "B" operand from
 // the tokens, so each lane's accumulators hold 4 consecutive outputs of one
 // token and leave as 8-byte stores.
 //
-// Data movement: the next K step is fetched from global memory into registers
-// (16 bytes a load, 8 consecutive lanes covering one 128-byte row segment)
-// while the matrix cores work on the current step from LDS; the registers are
-// then written to the other half of a double-buffered LDS (2 x 64 KiB), one
-// barrier per step.  Rows are stored in LDS as 8 chunks of 16 bytes with chunk
-// c of row r at position c ^ ((r & 7) ^ ((r >> 3) & 1)), so the 16-byte
-// fragment reads of 32 consecutive rows spread over all banks.
+// Data movement: global memory goes straight to LDS (buffer_load ... lds, 1
+// KiB a load, no register staging) into a 4-stage ring of 32 KiB stages, so
+// three K tiles are in flight while the matrix cores work on the fourth.
+// Each tile's two 16-MFMA sub-steps are issued as groups of 2 MFMAs + 1 LDS
+// fragment read of the next sub-step, with the next tile's loads spread one
+// per two groups; one workgroup barrier per tile.  Rows are stored in LDS as
+// 4 chunks of 16 bytes with chunk c of row r at c ^ swizzle(r), so the
+// 16-byte fragment reads of consecutive rows spread over all banks.
 //
 // Launch order: gfx950 dispatches consecutive workgroups to its 8 XCDs in
 // turn, each XCD with its own L2.  The workgroup id is remapped so that each
