@@ -184,6 +184,26 @@ def linear_bf16(x, w, nthreads: int = None) -> np.ndarray:
     return y
 
 
+def expand_q2k_matrix(blocks) -> np.ndarray:
+    """A weight matrix shipped as Q2_K blocks, [out, in/256, 84] uint8 -> its
+    bf16 expansion [out, in] (bits).  Block b of output row o holds that row's
+    weights [256b, 256b+256) and dequantises exactly as a table row does
+    (atlascybernetics "spark_model/layers/engram_v41.rs",
+    EngramLayerWeights::wkv_q2k: wkv as the GGUF ships it, whose one-token
+    projection gives the results of the bf16 expansion)."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    out_f, nb, nbytes = blocks.shape
+    assert nbytes == 84
+    rows = gather(blocks.reshape(out_f * nb, 84), None, np.arange(out_f * nb, dtype=np.int64))
+    return rows.reshape(out_f, nb * 256)
+
+
+def project_q2k(x, blocks, nthreads: int = None) -> np.ndarray:
+    """x [rows, in] bf16 bits through a Q2_K-shipped weight matrix: the
+    projection of the bf16 expansion ([metrale] linear_bf16)."""
+    return linear_bf16(x, expand_q2k_matrix(blocks), nthreads)
+
+
 def gate_and_add(h, kv, q_w, k_w, eps: float, round_bf16: bool = False,
                  nthreads: int = None) -> np.ndarray:
     """Returns the gated highway (a new f32 array) for h [T, hc, dim] f32,

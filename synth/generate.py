@@ -25,6 +25,10 @@ Recipe (one line per array):
 * e4m3 table: codes [rows, head_dim] uint8 = e4m3(clip(N(0,1), +-448));
   scales [rows, head_dim/scale_block] float32 = 2**k, k uniform in [k_lo, k_hi].
 * wkv [dim*(hc+1), cols*head_dim] bf16 bits = bf16(N(0, wkv_std)).
+* wkv as Q2_K blocks [dim*(hc+1), cols*head_dim/256, 84] uint8 (workloads with
+  wkv_fmt "q2k", instead of the bf16 wkv): bytes uniform; bytes 80..83
+  overwritten with fp16 d and dmin drawn from U(wkv_d_lo, wkv_d_hi), which puts
+  the dequantised weights at a spread of about 0.02.
 * q, k [hc, dim] bf16 bits = bf16(1 + qk_std*N(0,1)) each.
 * token ids [prompt + decode_steps] int32: uniform over the vocabulary, or
   Zipf(s) truncated to the vocabulary (pmf proportional to rank**-s) mapped
@@ -43,7 +47,8 @@ ROOT_SEED = 20261202
 CHUNK = 1 << 24            # elements per independently seeded chunk
 
 # spawn-key purposes
-_HASH, _TABLE, _SCALES, _WKV, _QK, _TOKENS, _HIGHWAY, _DECODE_HIGHWAY = range(8)
+_HASH, _TABLE, _SCALES, _WKV, _QK, _TOKENS, _HIGHWAY, _DECODE_HIGHWAY, _WKV_Q2K, \
+    _WKV_Q2K_SCALES = range(10)
 
 
 def _seq(entropy_idx: int, *key: int) -> np.random.SeedSequence:
@@ -162,6 +167,20 @@ def wkv(w: Workload, layer: int) -> np.ndarray:
     return _chunked(w.N * w.K, np.uint16, fill, w.family, _WKV, layer).reshape(w.N, w.K)
 
 
+def wkv_q2k(w: Workload, layer: int) -> np.ndarray:
+    """[N, K/256, 84] uint8 Q2_K blocks of wkv: uniform bytes, fp16 d/dmin in
+    U(wkv_d_lo, wkv_d_hi)."""
+    nb = w.N * (w.K // 256)
+    blk = _chunked(nb * 84, np.uint8, _fill_bytes, w.family, _WKV_Q2K, layer).reshape(nb, 84)
+
+    def fill_dd(g, dst):
+        dst[:] = g.uniform(w.wkv_d_lo, w.wkv_d_hi, size=dst.size).astype(np.float32)
+
+    dd = _chunked(nb * 2, np.float32, fill_dd, w.family, _WKV_Q2K_SCALES, layer)
+    blk[:, 80:84] = dd.astype(np.float16).view(np.uint8).reshape(nb, 4)
+    return blk.reshape(w.N, w.K // 256, 84)
+
+
 def qk_weights(w: Workload, layer: int):
     """(q, k), each [hc, dim] bf16 bits of 1 + qk_std * N(0, 1)."""
     g = _rng(w.family, _QK, layer)
@@ -200,7 +219,10 @@ def highway(w: Workload, T: int, decode: bool = False) -> np.ndarray:
 def layer_inputs(w: Workload, ht: dict, layer: int) -> dict:
     """Everything one engram layer needs besides the hash tables."""
     rows = int(ht["rows"][layer])
-    out = dict(rows=rows, wkv=wkv(w, layer))
+    if w.wkv_fmt == "q2k":
+        out = dict(rows=rows, wkv=None, wkv_q2k=wkv_q2k(w, layer))
+    else:
+        out = dict(rows=rows, wkv=wkv(w, layer), wkv_q2k=None)
     out["q"], out["k"] = qk_weights(w, layer)
     if w.fmt == "q2k":
         out["table"] = q2k_table(w, layer, rows)

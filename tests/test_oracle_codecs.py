@@ -220,3 +220,47 @@ def test_gather_bounds(orc):
         orc.gather(tab, None, np.array([-1]))
     rows = orc.gather(tab, None, np.array([[0, 3], [2, 1]]))
     assert rows.shape == (4, 256)
+
+
+# ------------------------------------------- wkv shipped as Q2_K blocks
+def test_expand_q2k_matrix_layout(orc):
+    """Block b of output row o must land on columns [256b, 256b+256) of row o.
+    Designed blocks: zero quants, min nibble 1, scale 0, dmin = (16o+b+1)/64,
+    so every value of block (o, b) is -(16o+b+1)/64 (exact in bf16)."""
+    out_f, nb = 3, 4
+    blocks = np.zeros((out_f, nb, 84), dtype=np.uint8)
+    for o in range(out_f):
+        for b in range(nb):
+            blocks[o, b] = encode_q2k(np.zeros(256, int), np.zeros(16, int), np.ones(16, int),
+                                      0.0, (16 * o + b + 1) / 64)
+    w = orc.f32_from_bf16(orc.expand_q2k_matrix(blocks))
+    assert w.shape == (out_f, nb * 256)
+    want = -(16 * np.arange(out_f)[:, None] + np.arange(nb * 256)[None, :] // 256 + 1) / 64
+    np.testing.assert_array_equal(w, want.astype(np.float32))
+
+
+def test_expand_q2k_matrix_values_within_block(orc):
+    """Inside a block the expansion follows the block's own value order: a block
+    whose quants count 0,1,2,3,0,... with scale 1, min 0, d 1 expands to that
+    count at every position of the row it sits in."""
+    Q = np.arange(256) % 4
+    blk = encode_q2k(Q, np.ones(16, int), np.zeros(16, int), 1.0, 0.0)
+    blocks = np.stack([np.stack([blk, blk])] * 2)          # [2, 2, 84]
+    w = orc.f32_from_bf16(orc.expand_q2k_matrix(blocks))
+    np.testing.assert_array_equal(w, np.tile(Q, (2, 2)).astype(np.float32))
+
+
+def test_project_q2k_contracts_over_inputs(orc):
+    """A one-hot token at input k returns column k of the expanded matrix, for
+    every output row (the input axis is the block axis, not the output axis)."""
+    rng = np.random.default_rng(11)
+    out_f, nb = 5, 3
+    blocks = rng.integers(0, 256, size=(out_f, nb, 84)).astype(np.uint8)
+    blocks[..., 80:84] = rng.uniform(1e-3, 2e-3, size=(out_f, nb, 2)).astype(
+        np.float16).view(np.uint8)
+    w = orc.expand_q2k_matrix(blocks)
+    for k in (0, 255, 256, 700):
+        x = np.zeros((1, nb * 256), dtype=np.float32)
+        x[0, k] = 1.0
+        y = orc.project_q2k(torch_bf16_bits(x).reshape(1, -1), blocks)
+        np.testing.assert_array_equal(y[0], w[:, k])

@@ -75,6 +75,13 @@ def test_table_recipes():
     dd = tab[:, 80:84].copy().view(np.float16).astype(np.float32)
     # fp16 rounding of U(1e-3, 1e-2): at most half an fp16 step outside
     assert dd.min() >= 1e-3 - 2 ** -21 and dd.max() <= 1e-2 + 2 ** -17
+    wq = synth.DECODE_WKVQ2K
+    blk = G.wkv_q2k(wq, 1)
+    assert blk.shape == (wq.N, wq.K // 256, 84) and blk.dtype == np.uint8
+    dd = blk[..., 80:84].copy().view(np.float16).astype(np.float32)
+    assert dd.min() >= 1e-3 - 2 ** -21 and dd.max() <= 2e-3 + 2 ** -20
+    np.testing.assert_array_equal(blk[7], G.wkv_q2k(wq, 1)[7])
+    assert not np.array_equal(blk[0], G.wkv_q2k(wq, 0)[0])
 
 
 def test_token_streams():
