@@ -23,8 +23,10 @@ STAGES = ("hash", "gather", "project", "gate")
 # Every symbol include/engram.h declares.
 EXPORTS = (
     "engram_last_error", "engram_abi_version", "engram_hash", "engram_gather_dequant",
-    "engram_project", "engram_qk_product", "engram_gate_apply", "engram_workspace_bytes",
-    "engram_ctx_create", "engram_ctx_add_layer", "engram_reset", "engram_forward",
+    "engram_project", "engram_project_q2k", "engram_dequant_q2k", "engram_qk_product",
+    "engram_gate_apply", "engram_workspace_bytes",
+    "engram_ctx_create", "engram_ctx_add_layer", "engram_ctx_set_wkv_q2k", "engram_reset",
+    "engram_forward",
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
     "engram_ctx_timing", "engram_ctx_destroy",
@@ -77,11 +79,14 @@ def lib():
             "engram_hash": (i32, [p, p, i64, i64, p, i64, p, p, p]),
             "engram_gather_dequant": (i32, [p, p, i64, i32, i64, p, p, p]),
             "engram_project": (i32, [p, p, p, i64, i64, i64, p]),
+            "engram_project_q2k": (i32, [p, p, p, i64, i64, i64, p]),
+            "engram_dequant_q2k": (i32, [p, i64, p, p]),
             "engram_qk_product": (i32, [p, p, p, i64, p]),
             "engram_gate_apply": (i32, [p, p, p, i64, i32, i64, ctypes.c_float, p]),
             "engram_workspace_bytes": (ctypes.c_size_t, [p]),
             "engram_ctx_create": (i32, [p, p, ctypes.c_size_t, p]),
             "engram_ctx_add_layer": (i32, [p, i32, p, p, p]),
+            "engram_ctx_set_wkv_q2k": (i32, [p, i32, p]),
             "engram_reset": (i32, [p, p]),
             "engram_forward": (i32, [p, i32, p, i64, p, p]),
             "engram_check": (i32, [p, p]),
@@ -176,6 +181,19 @@ def project(d_x, d_w, d_y, stream=None):
     _check(lib().engram_project(_ptr(d_x), _ptr(d_w), _ptr(d_y), T, K, N, _stream(stream)))
 
 
+def project_q2k(d_x, d_wq, d_y, stream=None):
+    """d_x [T, K] bf16 bits (T <= 1), d_wq [N, K/256, 84] uint8 Q2_K blocks."""
+    T, K = d_x.shape
+    N = d_wq.shape[0]
+    _check(lib().engram_project_q2k(_ptr(d_x), _ptr(d_wq), _ptr(d_y), T, K, N, _stream(stream)))
+
+
+def dequant_q2k(d_blocks, d_out, stream=None):
+    """Q2_K blocks (any shape [..., 84] uint8) -> d_out [n_blocks * 256] bf16 bits."""
+    n = d_blocks.numel() // 84
+    _check(lib().engram_dequant_q2k(_ptr(d_blocks), n, _ptr(d_out), _stream(stream)))
+
+
 def qk_product(d_q, d_k, d_qk, stream=None):
     _check(lib().engram_qk_product(_ptr(d_q), _ptr(d_k), _ptr(d_qk), int(d_q.numel()),
                                    _stream(stream)))
@@ -213,6 +231,12 @@ class Context:
         self._keep[hash_index] = (table, d_wkv, d_qk)
         _check(lib().engram_ctx_add_layer(self.h, hash_index, ctypes.byref(table.c),
                                           _ptr(d_wkv), _ptr(d_qk)))
+
+    def set_wkv_q2k(self, hash_index, d_wq):
+        """Registers (or, with None, drops) the layer's wkv as Q2_K blocks."""
+        table, wkv, qk = self._keep[hash_index][:3]
+        self._keep[hash_index] = (table, wkv, qk, d_wq)
+        _check(lib().engram_ctx_set_wkv_q2k(self.h, hash_index, _ptr(d_wq)))
 
     def reset(self, stream=None):
         _check(lib().engram_reset(self.h, _stream(stream)))

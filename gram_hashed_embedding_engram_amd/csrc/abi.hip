@@ -147,6 +147,26 @@ int32_t dispatch_project(const uint16_t *x, const uint16_t *w, uint16_t *y, int6
     return launch_gemm(x, w, y, T, K, N, l);
 }
 
+int32_t check_project_q2k(const uint16_t *x, const uint8_t *w, const uint16_t *y, int64_t T,
+                          int64_t K, int64_t N)
+{
+    CHECK(T >= 0, ENGRAM_E_ARG, "engram project_q2k: T = %lld", (long long)T);
+    CHECK(T <= 1, ENGRAM_E_UNSUPPORTED,
+          "engram project_q2k: one token per call (T = %lld); more take engram_project",
+          (long long)T);
+    CHECK(K >= 256 && K % 256 == 0 && K <= kQ2kWkvMaxK, ENGRAM_E_UNSUPPORTED,
+          "engram project_q2k: K = %lld must be a multiple of 256 up to %lld", (long long)K,
+          (long long)kQ2kWkvMaxK);
+    CHECK(N >= 1 && N < ((int64_t)1 << 31), ENGRAM_E_UNSUPPORTED,
+          "engram project_q2k: N = %lld", (long long)N);
+    if (T == 0)
+        return ENGRAM_OK;
+    CHECK(x && w && y, ENGRAM_E_ARG, "engram project_q2k: NULL pointer");
+    CHECK(aligned(x, 16) && aligned(w, 4) && aligned(y, 2), ENGRAM_E_ARG,
+          "engram project_q2k: x must be 16-byte, wkv_q2k 4-byte, y 2-byte aligned");
+    return ENGRAM_OK;
+}
+
 int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
                    int64_t dim, float eps)
 {
@@ -191,6 +211,7 @@ struct engram_ctx {
         bool set = false;
         engram_table tab{};
         const uint16_t *wkv = nullptr;
+        const uint8_t *wkv_q2k = nullptr;   // one-token projections read these if set
         const float *qk = nullptr;
     } layers[ENGRAM_MAX_LAYERS];
     int64_t pos = 0;
@@ -329,6 +350,28 @@ int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, 
     return dispatch_project(d_x, d_w, d_y, T, K, N, on(stream));
 }
 
+int32_t engram_project_q2k(const uint16_t *d_x, const uint8_t *d_wkv_q2k, uint16_t *d_y,
+                           int64_t T, int64_t K, int64_t N, void *stream)
+{
+    int32_t rc = check_project_q2k(d_x, d_wkv_q2k, d_y, T, K, N);
+    if (rc != ENGRAM_OK || T == 0)
+        return rc;
+    return launch_gemv_q2k(d_x, d_wkv_q2k, d_y, K, N, on(stream));
+}
+
+int32_t engram_dequant_q2k(const uint8_t *d_blocks, int64_t n_blocks, uint16_t *d_out,
+                           void *stream)
+{
+    CHECK(n_blocks >= 0 && n_blocks < ((int64_t)1 << 40), ENGRAM_E_ARG,
+          "engram dequant_q2k: %lld blocks", (long long)n_blocks);
+    if (n_blocks == 0)
+        return ENGRAM_OK;
+    CHECK(d_blocks && d_out, ENGRAM_E_ARG, "engram dequant_q2k: NULL pointer");
+    CHECK(aligned(d_blocks, 4) && aligned(d_out, 16), ENGRAM_E_ARG,
+          "engram dequant_q2k: blocks must be 4-byte, out 16-byte aligned");
+    return launch_dequant_q2k(d_blocks, n_blocks, d_out, on(stream));
+}
+
 int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk, int64_t n,
                           void *stream)
 {
@@ -428,7 +471,26 @@ int32_t engram_ctx_add_layer(engram_ctx *ctx, int32_t hash_index, const engram_t
     L.set = true;
     L.tab = *table;
     L.wkv = d_wkv;
+    L.wkv_q2k = nullptr;
     L.qk = d_qk;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_set_wkv_q2k(engram_ctx *ctx, int32_t hash_index, const uint8_t *d_wkv_q2k)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram set_wkv_q2k: NULL context");
+    CHECK(hash_index >= 0 && hash_index < ctx->nl, ENGRAM_E_ARG,
+          "engram set_wkv_q2k: hash index %d outside 0..%d", hash_index, ctx->nl - 1);
+    engram_ctx::Layer &L = ctx->layers[hash_index];
+    CHECK(L.set, ENGRAM_E_STATE, "engram set_wkv_q2k: layer %d has no weights", hash_index);
+    if (d_wkv_q2k) {
+        const int64_t K = (int64_t)ctx->cols * ctx->cfg.head_dim;
+        CHECK(K % 256 == 0 && K <= kQ2kWkvMaxK, ENGRAM_E_UNSUPPORTED,
+              "engram set_wkv_q2k: K = %lld must be a multiple of 256 up to %lld", (long long)K,
+              (long long)kQ2kWkvMaxK);
+        CHECK(aligned(d_wkv_q2k, 4), ENGRAM_E_ARG, "engram set_wkv_q2k: blocks must be 4-byte aligned");
+    }
+    L.wkv_q2k = d_wkv_q2k;
     return ENGRAM_OK;
 }
 
@@ -486,7 +548,8 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
         }
         rc = staged(ctx, 2, s, [&](const Launch &l) {
             return launch_decode(ctx->consts, cfg.hash.d_token_map, d_ids, ctx->step_start,
-                                 ctx->history, hash_index, hash_index == 0, L.tab, L.wkv, ctx->kv,
+                                 ctx->history, hash_index, hash_index == 0, L.tab, L.wkv,
+                                 L.wkv_q2k, ctx->kv,
                                  ctx->kv_width, ctx->row_ids, ctx->rows, ctx->err, l);
         });
         if (rc != ENGRAM_OK)
@@ -516,6 +579,8 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     if (rc != ENGRAM_OK)
         return rc;
     rc = staged(ctx, 2, s, [&](const Launch &l) {
+        if (T == 1 && L.wkv_q2k)
+            return launch_gemv_q2k(ctx->rows, L.wkv_q2k, ctx->kv, K, ctx->kv_width, l);
         return dispatch_project(ctx->rows, L.wkv, ctx->kv, T, K, ctx->kv_width, l);
     });
     if (rc != ENGRAM_OK)

@@ -173,6 +173,12 @@ int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T
                       int64_t id_stride, uint16_t *rows, int32_t *err, const Launch &l);
 int32_t launch_gemv(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,
                     int64_t N, const Launch &l);
+// One token through wkv given as Q2_K blocks [N][K/256][84] (gemv_q2k.hip).
+int32_t launch_gemv_q2k(const uint16_t *x, const uint8_t *w, uint16_t *y, int64_t K, int64_t N,
+                        const Launch &l);
+// Blocks 0..n_blocks-1 of a Q2_K array -> bf16 [n_blocks][256] (gather.hip).
+int32_t launch_dequant_q2k(const uint8_t *blocks, int64_t n_blocks, uint16_t *out,
+                           const Launch &l);
 int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t K,
                     int64_t N, const Launch &l);
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
@@ -186,11 +192,17 @@ int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
 // id comes from token_map[*ids] and is recorded in history[pos], and the row
 // ids of every layer are written to row_ids [n_layers][cols]; otherwise it is
 // read back from history[pos].  rows [cols*256] receives the dequantised rows.
+// w_q2k non-null: the projection reads wkv's Q2_K blocks [N][K/256][84]
+// instead of the bf16 w.
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
                       int64_t pos, int64_t *history, int32_t layer, bool first_layer,
-                      const engram_table &tab, const uint16_t *w, uint16_t *y, int64_t N,
-                      int64_t *row_ids, uint16_t *rows, int32_t *err, const Launch &l);
+                      const engram_table &tab, const uint16_t *w, const uint8_t *w_q2k,
+                      uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows, int32_t *err,
+                      const Launch &l);
 constexpr int64_t kDecodeMaxCols = 32;      // cols*256 <= 8192 activations in LDS
+
+// The Q2_K-wkv projection holds a token's activations for K <= 8192 in registers.
+constexpr int64_t kQ2kWkvMaxK = 8192;
 
 // GEMV covers T <= kGemvMaxT with K <= kGemvMaxK; larger T goes to the GEMM.
 constexpr int64_t kGemvMaxT = 4;

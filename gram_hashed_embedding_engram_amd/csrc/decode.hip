@@ -20,12 +20,16 @@
 // and the history entry, so the workspace holds what the separate stages
 // would have left there.
 //
+// With wkv registered as Q2_K blocks the projection loop is wkv_q2k.h's row
+// dot product instead (41 MB a layer instead of 252 MB): after the prologue
+// each lane copies its sub-blocks' activations from LDS into registers.
+//
 // The gate stays a launch of its own.  It needs every kv row, and doing it
 // in the last workgroup to finish was measured slower: the completion count
 // and the device-wide visibility of kv cost about 4 us per launch, and four
 // gate rows on one compute unit take twice as long as the gate kernel's
 // four workgroups.
-#include "common.h"
+#include "wkv_q2k.h"
 
 namespace engram {
 namespace {
@@ -33,23 +37,129 @@ namespace {
 constexpr int kDecodeBlocksPerCu = 4;
 constexpr int kMaxChunks = kDecodeMaxCols * 32;   // 8-value chunks of the activations
 
+// Everything a decode launch needs besides the hash constants and wkv.
+struct DecodeArgs {
+    const int64_t *token_map;
+    const int32_t *ids;
+    int64_t pos;
+    int64_t *history;
+    int32_t layer, first_layer;
+    const uint8_t *table;
+    const float *scales;
+    int64_t n_rows;
+    int32_t scale_block, reserved;
+    uint16_t *y;
+    int64_t N;
+    int64_t *row_ids;
+    uint16_t *rows;
+    int32_t *err;
+};
+
+// Hash of the token and gather + dequant of this layer's cols rows into the
+// activations s_x (every workgroup; workgroup 0 also writes the row ids, the
+// history entry and the dequantised rows).  Ends with s_x complete.
+template <int FMT>
+__device__ __forceinline__ void decode_prologue(const HashConsts &c, const DecodeArgs &a,
+                                                int64_t *s_id, uint32_t *s_blk, u32x4 *s_x)
+{
+    const int tid = threadIdx.x;
+    const int cols = c.cols;
+    const int64_t kc = (int64_t)cols * 32;
+    const int64_t pos = a.pos;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // ---- hash: thread (l, col) computes layer l's id of column col; every
+    // workgroup needs its own layer's, workgroup 0 of the first layer writes all
+    if (tid < c.nl * cols) {
+        const int l = tid / cols, col = tid - l * cols;
+        if (l == a.layer || (blockIdx.x == 0 && a.first_layer)) {
+            int64_t own;
+            bool bad = false;
+            if (a.first_layer) {
+                const int32_t t = a.ids[0];
+                bad = t < 0 || (int64_t)t >= c.vocab;
+                own = bad ? -1 : a.token_map[t];     // reported, then hashed as unmapped
+            } else {
+                own = a.history[pos];
+            }
+            const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
+            bool blocked = own == -1;
+            const int64_t *m = c.mult + l * c.ng;
+            uint64_t r = (uint64_t)(blocked ? c.pad_id : own) * (uint64_t)m[0];
+#pragma unroll
+            for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
+                if (k < ngram) {
+                    const int64_t q = pos - k;
+                    const int64_t src = q >= 0 ? a.history[q] : 0;
+                    blocked = blocked || q < 0 || src == -1;
+                    r ^= (uint64_t)(blocked ? c.pad_id : src) * (uint64_t)m[k];
+                }
+            }
+            const int slot = l * cols + col;
+            const int64_t id = rem_euclid((int64_t)r, c.prime[slot]) + c.offset[slot];
+            if (blockIdx.x == 0) {
+                a.row_ids[slot] = id;
+                if (tid == 0 && a.first_layer) {
+                    a.history[pos] = own;
+                    if (bad && a.err)
+                        atomicOr(a.err, ENGRAM_DEVERR_TOKEN);
+                }
+            }
+            if (l == a.layer) {
+                const bool in_table = id >= 0 && id < a.n_rows;
+                if (!in_table && blockIdx.x == 0 && a.err)
+                    atomicOr(a.err, ENGRAM_DEVERR_ROW);
+                s_id[col] = in_table ? id : -1;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gather + dequant of the cols rows into the activations in LDS
+    if (FMT == ENGRAM_FMT_Q2K) {
+        for (int i = tid; i < cols * 21; i += 256) {
+            const int r = i / 21, d = i - r * 21;
+            const int64_t id = s_id[r];
+            s_blk[i] = id >= 0 ? *(const uint32_t *)(a.table + id * ENGRAM_Q2K_ROW_BYTES + 4 * d)
+                               : 0u;
+        }
+        __syncthreads();
+        for (int ch = tid; ch < kc; ch += 256) {
+            const int r = ch >> 5;
+            s_x[ch] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
+        }
+    } else {
+        const int nb = 256 / a.scale_block;
+        for (int ch = tid; ch < kc; ch += 256) {
+            const int r = ch >> 5, sub = ch & 31;
+            const int64_t id = s_id[r];
+            u32x4 o = zero;
+            if (id >= 0) {
+                const uint32_t *b = (const uint32_t *)(a.table + id * 256 + 8 * sub);
+                o = e4m3_dequant8(b[0], b[1], a.scales[id * nb + (8 * sub) / a.scale_block]);
+            }
+            s_x[ch] = o;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int ch = tid; ch < kc; ch += 256)
+            ((u32x4 *)a.rows)[ch] = s_x[ch];
+}
+
 template <int FMT, int NI>
-__global__ __launch_bounds__(256) void decode_kernel(
-    const HashConsts c, const int64_t *__restrict__ token_map, const int32_t *__restrict__ ids,
-    int64_t pos, int64_t *__restrict__ history, int layer, int first_layer,
-    const uint8_t *__restrict__ table, const float *__restrict__ scales, int64_t n_rows,
-    int scale_block, const uint16_t *__restrict__ w, uint16_t *__restrict__ y, int64_t N,
-    int64_t *__restrict__ row_ids, uint16_t *__restrict__ rows, int32_t *__restrict__ err)
+__global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const DecodeArgs a,
+                                                     const uint16_t *__restrict__ w)
 {
     __shared__ int64_t s_id[kDecodeMaxCols];
     __shared__ uint32_t s_blk[kDecodeMaxCols * 21];
     __shared__ u32x4 s_x[kMaxChunks];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int cols = c.cols;
-    const int64_t K = (int64_t)cols * 256, kc = K >> 3;
+    const int64_t K = (int64_t)c.cols * 256, kc = K >> 3, N = a.N;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint16_t *__restrict__ y = a.y;
 
     // ---- the first wkv row of this wavefront goes out before anything else
     u32x4 wv[NI];
@@ -62,82 +172,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         }
     }
 
-    // ---- hash: thread (l, col) computes layer l's id of column col; every
-    // workgroup needs its own layer's, workgroup 0 of the first layer writes all
-    if (tid < c.nl * cols) {
-        const int l = tid / cols, col = tid - l * cols;
-        if (l == layer || (blockIdx.x == 0 && first_layer)) {
-            int64_t own;
-            bool bad = false;
-            if (first_layer) {
-                const int32_t t = ids[0];
-                bad = t < 0 || (int64_t)t >= c.vocab;
-                own = bad ? -1 : token_map[t];       // reported, then hashed as unmapped
-            } else {
-                own = history[pos];
-            }
-            const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
-            bool blocked = own == -1;
-            const int64_t *m = c.mult + l * c.ng;
-            uint64_t r = (uint64_t)(blocked ? c.pad_id : own) * (uint64_t)m[0];
-#pragma unroll
-            for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
-                if (k < ngram) {
-                    const int64_t q = pos - k;
-                    const int64_t src = q >= 0 ? history[q] : 0;
-                    blocked = blocked || q < 0 || src == -1;
-                    r ^= (uint64_t)(blocked ? c.pad_id : src) * (uint64_t)m[k];
-                }
-            }
-            const int slot = l * cols + col;
-            const int64_t id = rem_euclid((int64_t)r, c.prime[slot]) + c.offset[slot];
-            if (blockIdx.x == 0) {
-                row_ids[slot] = id;
-                if (tid == 0 && first_layer) {
-                    history[pos] = own;
-                    if (bad && err)
-                        atomicOr(err, ENGRAM_DEVERR_TOKEN);
-                }
-            }
-            if (l == layer) {
-                const bool in_table = id >= 0 && id < n_rows;
-                if (!in_table && blockIdx.x == 0 && err)
-                    atomicOr(err, ENGRAM_DEVERR_ROW);
-                s_id[col] = in_table ? id : -1;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- gather + dequant of the cols rows into the activations in LDS
-    if (FMT == ENGRAM_FMT_Q2K) {
-        for (int i = tid; i < cols * 21; i += 256) {
-            const int r = i / 21, d = i - r * 21;
-            const int64_t id = s_id[r];
-            s_blk[i] = id >= 0 ? *(const uint32_t *)(table + id * ENGRAM_Q2K_ROW_BYTES + 4 * d) : 0u;
-        }
-        __syncthreads();
-        for (int ch = tid; ch < kc; ch += 256) {
-            const int r = ch >> 5;
-            s_x[ch] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
-        }
-    } else {
-        const int nb = 256 / scale_block;
-        for (int ch = tid; ch < kc; ch += 256) {
-            const int r = ch >> 5, sub = ch & 31;
-            const int64_t id = s_id[r];
-            u32x4 o = zero;
-            if (id >= 0) {
-                const uint32_t *b = (const uint32_t *)(table + id * 256 + 8 * sub);
-                o = e4m3_dequant8(b[0], b[1], scales[id * nb + (8 * sub) / scale_block]);
-            }
-            s_x[ch] = o;
-        }
-    }
-    __syncthreads();
-    if (blockIdx.x == 0)
-        for (int ch = tid; ch < kc; ch += 256)
-            ((u32x4 *)rows)[ch] = s_x[ch];
+    decode_prologue<FMT>(c, a, s_id, s_blk, s_x);
 
     // ---- projection: rows wave, wave + n_waves, ...  A row's result is
     // stored after the next row's loads are issued, so the loop's wait for
@@ -170,12 +205,61 @@ __global__ __launch_bounds__(256) void decode_kernel(
         y[prev_n] = prev_v;
 }
 
+// The same layer step with wkv as Q2_K blocks [N][K/256][84].
+template <int FMT, int NSB>
+__global__ __launch_bounds__(256) void decode_q2kw_kernel(const HashConsts c, const DecodeArgs a,
+                                                          const uint8_t *__restrict__ wq)
+{
+    constexpr int NLD = q2k_row_loads<NSB>();
+    __shared__ int64_t s_id[kDecodeMaxCols];
+    __shared__ uint32_t s_blk[kDecodeMaxCols * 21];
+    __shared__ u32x4 s_x[kMaxChunks];
+    __shared__ uint32_t s_row[4][kQ2kWkvMaxRowDwords];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int K = c.cols * 256, n_sb = K >> 4, row_dwords = 21 * (K >> 8);
+    const int64_t N = a.N;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const uint32_t *wd = (const uint32_t *)wq;
+
+    // ---- the first row's blocks go out before anything else
+    uint32_t r[NLD];
+    q2k_row_load<NLD>(wd + min(wave, N - 1) * row_dwords, row_dwords, lane, r);
+
+    decode_prologue<FMT>(c, a, s_id, s_blk, s_x);
+
+    // ---- this lane's sub-blocks of the activations, into registers
+    uint32_t xr[NSB][8];
+#pragma unroll
+    for (int i = 0; i < NSB; i++) {
+        const int g = lane + 64 * i;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
+        if (g < n_sb) {
+            lo = s_x[2 * g];
+            hi = s_x[2 * g + 1];
+        }
+        xr[i][0] = lo.x; xr[i][1] = lo.y; xr[i][2] = lo.z; xr[i][3] = lo.w;
+        xr[i][4] = hi.x; xr[i][5] = hi.y; xr[i][6] = hi.z; xr[i][7] = hi.w;
+    }
+
+    // ---- projection, one row per wavefront at a time
+    for (int64_t n = wave; n < N; n += n_waves) {
+        q2k_row_stage<NLD>(s_row[wid], r, row_dwords, lane);
+        if (n + n_waves < N)
+            q2k_row_load<NLD>(wd + (n + n_waves) * row_dwords, row_dwords, lane, r);
+        const float s = wave_sum(q2k_row_dot<NSB>(s_row[wid], xr, n_sb, lane));
+        if (lane == 0)
+            a.y[n] = f32_to_bf16(s);
+    }
+}
+
 }  // namespace
 
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
                       int64_t pos, int64_t *history, int32_t layer, bool first_layer,
-                      const engram_table &tab, const uint16_t *w, uint16_t *y, int64_t N,
-                      int64_t *row_ids, uint16_t *rows, int32_t *err, const Launch &l)
+                      const engram_table &tab, const uint16_t *w, const uint8_t *w_q2k,
+                      uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows, int32_t *err,
+                      const Launch &l)
 {
     static int cus = 0;
     if (cus == 0) {
@@ -185,24 +269,45 @@ int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32
             cus <= 0)
             cus = 256;
     }
+    const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
+                       tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
+                       row_ids, rows, err};
     const int64_t K = (int64_t)c.cols * 256;
-    const int64_t ni = (K + 511) / 512;
     int64_t blocks = (N + 3) / 4;
     const int64_t cap = (int64_t)cus * kDecodeBlocksPerCu;
     if (blocks > cap)
         blocks = cap;
     const dim3 grid((unsigned)blocks), block(256);
+    const bool q2k_table = tab.fmt == ENGRAM_FMT_Q2K;
+    if (w_q2k) {
+        const int nsb = (int)((K + 1023) / 1024);
+#define ENGRAM_DECODE_Q2KW_CASE(S_)                                                              \
+    case S_:                                                                                     \
+        if (q2k_table)                                                                           \
+            dispatch(decode_q2kw_kernel<ENGRAM_FMT_Q2K, S_>, grid, block, l, true, true, c, a,   \
+                     w_q2k);                                                                     \
+        else                                                                                     \
+            dispatch(decode_q2kw_kernel<ENGRAM_FMT_E4M3, S_>, grid, block, l, true, true, c, a,  \
+                     w_q2k);                                                                     \
+        break;
+        switch (nsb) {
+            ENGRAM_DECODE_Q2KW_CASE(1) ENGRAM_DECODE_Q2KW_CASE(2) ENGRAM_DECODE_Q2KW_CASE(3)
+            ENGRAM_DECODE_Q2KW_CASE(4) ENGRAM_DECODE_Q2KW_CASE(5) ENGRAM_DECODE_Q2KW_CASE(6)
+            ENGRAM_DECODE_Q2KW_CASE(7) ENGRAM_DECODE_Q2KW_CASE(8)
+        default:
+            return fail(ENGRAM_E_UNSUPPORTED, "engram decode: %lld columns exceed %lld",
+                        (long long)c.cols, (long long)kDecodeMaxCols);
+        }
+#undef ENGRAM_DECODE_Q2KW_CASE
+        return launch_status("engram decode kernel");
+    }
+    const int64_t ni = (K + 511) / 512;
 #define ENGRAM_DECODE_CASE(NI_)                                                                  \
     case NI_:                                                                                    \
-        if (tab.fmt == ENGRAM_FMT_Q2K)                                                           \
-            dispatch(decode_kernel<ENGRAM_FMT_Q2K, NI_>, grid, block, l, true, true, c, token_map, \
-                     ids, pos, history, (int)layer, (int)first_layer, tab.d_data, tab.d_scales,  \
-                     tab.n_rows, (int)tab.scale_block, w, y, N, row_ids, rows, err);             \
+        if (q2k_table)                                                                           \
+            dispatch(decode_kernel<ENGRAM_FMT_Q2K, NI_>, grid, block, l, true, true, c, a, w);   \
         else                                                                                     \
-            dispatch(decode_kernel<ENGRAM_FMT_E4M3, NI_>, grid, block, l, true, true, c,         \
-                     token_map, ids, pos, history, (int)layer, (int)first_layer, tab.d_data,     \
-                     tab.d_scales, tab.n_rows, (int)tab.scale_block, w, y, N, row_ids, rows,     \
-                     err);                                                                       \
+            dispatch(decode_kernel<ENGRAM_FMT_E4M3, NI_>, grid, block, l, true, true, c, a, w);  \
         break;
     switch (ni) {
         ENGRAM_DECODE_CASE(1) ENGRAM_DECODE_CASE(2) ENGRAM_DECODE_CASE(3) ENGRAM_DECODE_CASE(4)

@@ -5,7 +5,8 @@
 //
 // Output row r = t*cols + c holds table row ids[t*id_stride + c]; the rows of
 // one token are contiguous, so the output is the [T, cols*head_dim] input of
-// the projection.
+// the projection.  Without ids the Q2_K kernel expands blocks 0..T-1 in order
+// (the bf16 expansion of a weight matrix shipped as Q2_K blocks).
 //
 // Q2_K (84-byte blocks, only 4-byte aligned): a workgroup takes 64 rows at a
 // time.  It first stages the 64 blocks in LDS with one coalesced dword load
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void gather_q2k_kernel(const uint8_t *__restri
             if (r < total_rows) {
                 const int64_t t = r / cols;
                 const int64_t c = r - t * cols;
-                const int64_t id = ids[t * id_stride + c];
+                const int64_t id = ids ? ids[t * id_stride + c] : r;
                 if (id >= 0 && id < n_table_rows)
                     off = id * ENGRAM_Q2K_ROW_BYTES;
                 else if (err)
@@ -144,6 +145,19 @@ int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T
                  total_rows, rows, err);
     }
     return launch_status("engram gather kernel");
+}
+
+int32_t launch_dequant_q2k(const uint8_t *blocks, int64_t n_blocks, uint16_t *out,
+                           const Launch &l)
+{
+    if (n_blocks == 0)
+        return ENGRAM_OK;
+    int64_t grid = (n_blocks + kQ2kRows - 1) / kQ2kRows;
+    if (grid > 16384)
+        grid = 16384;
+    dispatch(gather_q2k_kernel, dim3((unsigned)grid), dim3(256), l, true, true, blocks, n_blocks,
+             (const int64_t *)nullptr, (int64_t)1, (int32_t)1, n_blocks, out, (int32_t *)nullptr);
+    return launch_status("engram dequant kernel");
 }
 
 }  // namespace engram

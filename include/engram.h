@@ -162,6 +162,29 @@ int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_id
 int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
                        int64_t K, int64_t N, void *stream);
 
+/* The same projection for one token with the weight matrix given as Q2_K
+ * blocks, as the GGUF ships wkv (atlascybernetics "engram_v41.rs",
+ * EngramLayerWeights::wkv_q2k and EngramV41's single-token projection over
+ * the raw blocks: 84 bytes per 256 weights instead of 512).  Weight k of
+ * output row n is value k%256 of block k/256 of that row, decoded as a table
+ * row is (bf16(d*scale*q - dmin*min)); the sum is f32, rounded once to bf16.
+ * Results agree with engram_project over the bf16 expansion
+ * (engram_dequant_q2k) to the rounding of the f32 sum, not bit for bit: the
+ * two kernels add in different orders.
+ *   d_x [T][K] bf16 (16-byte aligned), d_wkv_q2k [N][K/256][84] (4-byte
+ *   aligned), d_y [T][N] bf16; T in 0..1 (more tokens: ENGRAM_E_UNSUPPORTED,
+ *   use engram_project); K a multiple of 256 up to 8192. */
+int32_t engram_project_q2k(const uint16_t *d_x, const uint8_t *d_wkv_q2k, uint16_t *d_y,
+                           int64_t T, int64_t K, int64_t N, void *stream);
+
+/* Blocks 0..n_blocks-1 of a Q2_K array -> bf16 [n_blocks][256], each decoded
+ * as a table row (atlascybernetics "engram_v41.rs", the dequant_q2_k_to_bf16
+ * kernel EngramV41 holds): the bf16 expansion of a weight matrix shipped as
+ * Q2_K blocks, for the many-token GEMM.  d_blocks 4-byte, d_out 16-byte
+ * aligned. */
+int32_t engram_dequant_q2k(const uint8_t *d_blocks, int64_t n_blocks, uint16_t *d_out,
+                           void *stream);
+
 /* ------------------------------------------------------------------- gate */
 
 /* qk[i] = f32(q[i]) * f32(k[i]) for n values (atlascybernetics
@@ -219,9 +242,18 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
  * [cols*head_dim] bf16 and qk [hc][dim] f32 (atlascybernetics
  * "engram_v41.rs", add_layer and EngramLayerWeights).  Refuses a table with
  * fewer rows than max(offset + prime) of that layer, so every hashed id is a
- * valid row.  Re-registering replaces the layer's pointers. */
+ * valid row.  Re-registering replaces the layer's pointers (and drops its
+ * Q2_K wkv). */
 int32_t engram_ctx_add_layer(engram_ctx *ctx, int32_t hash_index, const engram_table *table,
                              const uint16_t *d_wkv, const float *d_qk);
+
+/* Registers the layer's wkv also as Q2_K blocks [dim*(hc+1)][K/256][84]
+ * (atlascybernetics "engram_v41.rs", EngramLayerWeights::wkv_q2k; NULL drops
+ * them): every one-token forward of the layer then projects from these
+ * blocks (engram_project_q2k's arithmetic) and the bf16 wkv serves T > 1.
+ * The layer must be registered; K = cols*head_dim a multiple of 256 up to
+ * 8192; blocks 4-byte aligned and caller-owned. */
+int32_t engram_ctx_set_wkv_q2k(engram_ctx *ctx, int32_t hash_index, const uint8_t *d_wkv_q2k);
 
 /* History := 0, position := 0, device error word := 0, no step open. */
 int32_t engram_reset(engram_ctx *ctx, void *stream);

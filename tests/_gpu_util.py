@@ -57,12 +57,22 @@ class Device:
         self.token_map = torch.from_numpy(self.ht["token_map"]).to(dev)
         self.tables = E.HashTables(self.token_map, self.ht["pad_id"], self.ht["multipliers"],
                                    self.ht["primes"], self.ht["offsets"])
-        self.tab, self.wkv, self.qk = [], [], []
+        self.tab, self.wkv, self.wkvq, self.qk = [], [], [], []
+        self._oracle_wkv = {}
         for L in self.layers:
             data = torch.from_numpy(L["table"]).to(dev)
             scales = None if L["scales"] is None else torch.from_numpy(L["scales"]).to(dev)
             self.tab.append(E.Table(data, scales, head_dim=w.head_dim, scale_block=w.scale_block))
-            self.wkv.append(torch.from_numpy(L["wkv"].view(np.int16)).to(dev))
+            if L["wkv_q2k"] is None:
+                self.wkv.append(torch.from_numpy(L["wkv"].view(np.int16)).to(dev))
+                self.wkvq.append(None)
+            else:
+                # wkv shipped as Q2_K blocks: the library expands them for T > 1
+                blocks = torch.from_numpy(L["wkv_q2k"]).to(dev)
+                bf = torch.empty(w.N, w.K, dtype=torch.int16, device=dev)
+                E.dequant_q2k(blocks, bf)
+                self.wkv.append(bf)
+                self.wkvq.append(blocks)
             q = torch.from_numpy(L["q"].view(np.int16)).to(dev)
             k = torch.from_numpy(L["k"].view(np.int16)).to(dev)
             qk = torch.empty(w.hc, w.dim, dtype=torch.float32, device=dev)
@@ -76,8 +86,20 @@ class Device:
         ctx = E.Context(self.tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
         for l in range(w.n_layers):
             ctx.add_layer(l, self.tab[l], self.wkv[l], self.qk[l])
+            if self.wkvq[l] is not None:
+                ctx.set_wkv_q2k(l, self.wkvq[l])
         ctx.reset()
         return ctx
+
+    def oracle_wkv(self, layer):
+        """The layer's bf16 wkv as the oracle sees it: the stored matrix, or
+        the oracle's expansion of the Q2_K blocks."""
+        import oracle
+        if layer not in self._oracle_wkv:
+            L = self.layers[layer]
+            self._oracle_wkv[layer] = (L["wkv"] if L["wkv_q2k"] is None
+                                       else oracle.expand_q2k_matrix(L["wkv_q2k"]))
+        return self._oracle_wkv[layer]
 
     def oracle_hasher(self, max_seq):
         import oracle

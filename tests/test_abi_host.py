@@ -121,6 +121,25 @@ def test_project_refusals(L):
     assert L.engram_project(FAKE, FAKE, FAKE, 0, 6144, 20480, None) == E.OK
 
 
+def test_project_q2k_refusals(L):
+    f = L.engram_project_q2k
+    assert f(FAKE, FAKE, FAKE, 2, 6144, 20480, None) == E.E_UNSUPPORTED     # one token only
+    assert f(FAKE, FAKE, FAKE, 1, 6000, 20480, None) == E.E_UNSUPPORTED     # K % 256
+    assert f(FAKE, FAKE, FAKE, 1, 8448, 20480, None) == E.E_UNSUPPORTED     # K > 8192
+    assert f(FAKE, FAKE, FAKE, 1, 6144, 0, None) == E.E_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, -1, 6144, 20480, None) == E.E_ARG
+    assert f(None, FAKE, FAKE, 1, 6144, 20480, None) == E.E_ARG
+    assert f(FAKE + 8, FAKE, FAKE, 1, 6144, 20480, None) == E.E_ARG        # x 16-byte
+    assert f(FAKE, FAKE + 2, FAKE, 1, 6144, 20480, None) == E.E_ARG        # blocks 4-byte
+    assert f(None, None, None, 0, 6144, 20480, None) == E.OK
+    d = L.engram_dequant_q2k
+    assert d(FAKE, -1, FAKE, None) == E.E_ARG
+    assert d(None, 3, FAKE, None) == E.E_ARG
+    assert d(FAKE + 2, 3, FAKE, None) == E.E_ARG
+    assert d(FAKE, 3, FAKE + 8, None) == E.E_ARG
+    assert d(None, 0, None, None) == E.OK
+
+
 def test_gate_refusals(L):
     f = lambda T=4, hc=4, dim=4096, eps=1e-6, h=FAKE: L.engram_gate_apply(
         h, FAKE, FAKE, T, hc, dim, ctypes.c_float(eps), None)
@@ -169,7 +188,9 @@ def test_context_refusals_and_state(L):
         hist, rid, rows, kv, err = FAKE, *[p.value for p in ptrs]
         assert rid == FAKE + 4096 and rows == rid + 8 * 64 * 48
         assert err == FAKE + n - 256
-        # forward before any layer is registered
+        # forward / Q2_K wkv before any layer is registered
+        rc, msg = rc_msg(L.engram_ctx_set_wkv_q2k(h, 0, FAKE))
+        assert rc == E.E_STATE and "no weights" in msg
         rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 1, FAKE, None))
         assert rc == E.E_STATE and "no weights" in msg
         # the table must cover every hashed id of the layer: max(offset+prime) =
@@ -193,6 +214,12 @@ def test_context_refusals_and_state(L):
         assert L.engram_forward(h, 0, None, 1, FAKE, None) == E.E_ARG
         assert L.engram_forward(h, 0, FAKE, 1, FAKE + 4, None) == E.E_ARG
         assert L.engram_forward(h, 3, FAKE, 1, FAKE, None) == E.E_ARG
+        # Q2_K wkv: an unregistered layer, misaligned blocks; NULL drops them
+        assert L.engram_ctx_set_wkv_q2k(h, 1, FAKE) == E.OK
+        rc, msg = rc_msg(L.engram_ctx_set_wkv_q2k(h, 2, FAKE))
+        assert rc == E.E_ARG
+        assert L.engram_ctx_set_wkv_q2k(h, 0, FAKE + 2) == E.E_ARG
+        assert L.engram_ctx_set_wkv_q2k(h, 0, None) == E.OK
         # a valid call before the first engram_reset (nothing is launched)
         rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 1, FAKE, None))
         assert rc == E.E_STATE and "engram_reset" in msg

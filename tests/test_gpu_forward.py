@@ -47,11 +47,11 @@ def check_call(dev, ctx, layer, ids_np, hasher_out, h_before, h_after, T, sample
     np.testing.assert_array_equal(rows, want_rows, err_msg=f"{label} rows")
     kv = to_np_u16(kv)
     toks = np.arange(T) if sample_tokens is None else sample_tokens
-    want_kv = oracle.linear_bf16(rows[toks], dev.layers[layer]["wkv"])
+    want_kv = oracle.linear_bf16(rows[toks], dev.oracle_wkv(layer))
     e_kv = relerr(widen(kv[toks]), widen(want_kv))
     assert e_kv <= 1e-2, f"{label} kv relerr {e_kv:.2e}"
     if sample_cols is not None:
-        want_c = oracle.linear_bf16(rows, dev.layers[layer]["wkv"][sample_cols])
+        want_c = oracle.linear_bf16(rows, dev.oracle_wkv(layer)[sample_cols])
         e_c = relerr(widen(kv[:, sample_cols]), widen(want_c))
         assert e_c <= 1e-2, f"{label} kv cols relerr {e_c:.2e}"
     L = dev.layers[layer]
@@ -77,7 +77,7 @@ def test_forward_tiny(E):
     e_kv, e_h, kv = check_call(dev, ctx, 0, ids, want_ids, h0, h1, 64, label="tiny")
     # the fully oracle chain (diagnostic: differs from the GPU's by kv rounding)
     rows = dev.oracle_rows(0, want_ids[:, 0, :]).reshape(64, -1)
-    kv_o = oracle.linear_bf16(rows, dev.layers[0]["wkv"])
+    kv_o = oracle.linear_bf16(rows, dev.oracle_wkv(0))
     h_o = oracle.gate_and_add(h0, kv_o, dev.layers[0]["q"], dev.layers[0]["k"], w.eps)
     log(f"  kv {e_kv:.2e}  highway {e_h:.2e}  full-oracle highway {relerr(h1, h_o):.2e}"
         f"  kv bits differing {(kv != kv_o).mean():.2e}")
@@ -112,6 +112,40 @@ def test_forward_decode_workload(E):
             worst = [max(worst[0], e_kv), max(worst[1], e_h)]
         pos += T
         assert ctx.position == pos
+    ctx.check()
+    log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
+
+
+def test_forward_decode_wkv_q2k(E):
+    """The decode workload with wkv shipped as Q2_K blocks: the 32-token prompt
+    runs the GEMM over the library's bf16 expansion, every single-token step
+    projects from the blocks; kv against the oracle projection over the
+    oracle's own expansion."""
+    w = synth.DECODE_WKVQ2K
+    steps = 64
+    log(f"forward: decode Q2_K with Q2_K wkv, prompt 32 + {steps} steps, 2 layers")
+    dev = Device(w.name)
+    ids = G.token_ids(w)
+    max_seq = w.prompt + steps
+    ctx = dev.context(max_tokens=32, max_seq=max_seq)
+    hasher = dev.oracle_hasher(max_seq)
+    d_ids = cuda(ids.astype(np.int32))
+    prompt_h = G.highway(w, w.prompt)
+    step_h = G.highway(w, steps, decode=True)
+    worst = [0.0, 0.0]
+    pos = 0
+    for step in range(1 + steps):
+        T = w.prompt if step == 0 else 1
+        h0 = prompt_h if step == 0 else step_h[step - 1:step]
+        want_ids = hasher.hash(ids[pos:pos + T], pos)
+        for layer in range(2):
+            d_h = torch.from_numpy(h0).cuda()
+            ctx.forward(layer, d_ids[pos:pos + T] if layer == 0 else None, T, d_h)
+            h1 = d_h.cpu().numpy()
+            e_kv, e_h, _ = check_call(dev, ctx, layer, ids[pos:pos + T], want_ids, h0, h1, T,
+                                      label=f"step {step} layer {layer}")
+            worst = [max(worst[0], e_kv), max(worst[1], e_h)]
+        pos += T
     ctx.check()
     log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
 
@@ -237,7 +271,8 @@ def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
     return out
 
 
-@pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name])
+@pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name,
+                                  synth.DECODE_WKVQ2K.name])
 def test_fused_decode_matches_staged(E, name):
     """The one-launch decode layer (hash + gather + projection) leaves exactly
     what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""

@@ -249,6 +249,86 @@ def test_project_gemm_full_shape(E, decode, M):
     check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
 
 
+# ---------------------------------------------- projection off Q2_K wkv
+def q2k_blocks(rng, n_out, nb):
+    """Random Q2_K weight blocks [n_out, nb, 84] with fp16 d, dmin in the
+    Q2_K-wkv recipe's range."""
+    blk = rng.integers(0, 256, size=(n_out, nb, 84)).astype(np.uint8)
+    blk[..., 80:84] = rng.uniform(1e-3, 2e-3, size=(n_out, nb, 2)).astype(
+        np.float16).view(np.uint8)
+    return blk
+
+
+def test_dequant_q2k_exact(E):
+    """The library's expansion of a Q2_K weight array equals the oracle's,
+    bit for bit: a slice of the decode-shape wkv (984 blocks, not a multiple
+    of the 64 a workgroup stages) and blocks with extreme fp16 scales."""
+    import oracle
+    w = synth.DECODE_WKVQ2K
+    blocks = G.wkv_q2k(w, 0)[:41]                         # [41, 24, 84]
+    rng = np.random.default_rng(5)
+    extra = rng.integers(0, 256, size=(7, 84)).astype(np.uint8)
+    for i, (d, dmin) in enumerate(((6e-8, 3e-8), (60000.0, 1.0), (1.0, 60000.0),
+                                   (-2.0, 0.5), (0.0, 0.0), (1e-3, -1e-3), (65504.0, 65504.0))):
+        extra[i, 80:82] = np.array([d], dtype=np.float16).view(np.uint8)
+        extra[i, 82:84] = np.array([dmin], dtype=np.float16).view(np.uint8)
+    flat = np.concatenate([blocks.reshape(-1, 84), extra])
+    out = torch.empty(flat.shape[0] * 256, dtype=torch.int16, device="cuda")
+    log(f"dequant_q2k: {flat.shape[0]} blocks")
+    E.dequant_q2k(torch.from_numpy(flat).cuda(), out)
+    want = oracle.expand_q2k_matrix(flat[:, None, :]).reshape(-1)
+    np.testing.assert_array_equal(to_np_u16(out), want)
+
+
+def check_project_q2k(E, x, blocks_host, blocks_dev=None, expanded=None, sample=None):
+    import oracle
+    K = x.shape[1]
+    N = blocks_host.shape[0]
+    if blocks_dev is None:
+        blocks_dev = torch.from_numpy(np.ascontiguousarray(blocks_host)).cuda()
+    y = torch.empty(1, N, dtype=torch.int16, device="cuda")
+    E.project_q2k(cuda(x), blocks_dev, y)
+    got = to_np_u16(y)[0]
+    rows = np.arange(N) if sample is None else sample
+    w = oracle.expand_q2k_matrix(blocks_host[rows]) if expanded is None else expanded[rows]
+    want = oracle.linear_bf16(x, w)[0]
+    e = relerr(widen(got[rows]), widen(want))
+    diff = (got[rows] != want).mean()
+    log(f"  relerr {e:.2e}, {diff:.2e} of outputs differ from the oracle's bits")
+    assert e <= 1e-2
+    return got
+
+
+def test_project_q2k_decode_shape(E):
+    """One token of dequantised table rows through the decode-shape Q2_K wkv
+    (K 6144, N 20480), every output checked."""
+    import oracle
+    w = synth.DECODE_WKVQ2K
+    dev = Device(w.name)
+    rng = np.random.default_rng(21)
+    ids = rng.integers(0, dev.layers[0]["rows"], size=(1, 24))
+    x = dev.oracle_rows(0, ids).reshape(1, -1)
+    log("project_q2k: K=6144 N=20480")
+    check_project_q2k(E, x, dev.layers[0]["wkv_q2k"], dev.wkvq[0], dev.oracle_wkv(0))
+
+
+@pytest.mark.parametrize("K,N", [(256, 7), (1280, 1000), (1024, 1), (8192, 515), (3072, 4097)])
+def test_project_q2k_ragged(E, K, N):
+    """K from one block to the 8192 limit (lanes left idle, partial sub-block
+    rounds) and N not a multiple of the wavefronts in the grid."""
+    rng = np.random.default_rng(K + N)
+    blocks = q2k_blocks(rng, N, K // 256)
+    x = bf16_rand(rng, (1, K), 1.0)
+    log(f"project_q2k: K={K} N={N}")
+    check_project_q2k(E, x, blocks)
+
+
+def test_project_q2k_empty(E):
+    x = torch.empty(0, 1024, dtype=torch.int16, device="cuda")
+    y = torch.empty(0, 64, dtype=torch.int16, device="cuda")
+    E.project_q2k(x, torch.empty(64, 4, 84, dtype=torch.uint8, device="cuda"), y)
+
+
 def test_project_empty(E, tiny):
     x = torch.empty(0, tiny.w.K, dtype=torch.int16, device="cuda")
     y = torch.empty(0, tiny.w.N, dtype=torch.int16, device="cuda")
