@@ -99,10 +99,35 @@ def device_inputs(w, torch, E, G):
 
 def make_ctx(E, w, tables, layers, max_tokens, max_seq):
     ctx = E.Context(tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
-    for l, (tab, wkv, qk) in enumerate(layers):
+    for l, layer in enumerate(layers):
+        tab, wkv, qk = layer[:3]
         ctx.add_layer(l, tab, wkv, qk)
+        if len(layer) > 3:
+            ctx.set_wkv_q2k(l, layer[3])
     ctx.reset()
     return ctx
+
+
+def wkv_q2k_inputs(w, inputs, torch, E, G):
+    """The decode inputs with each layer's wkv shipped as Q2_K blocks: the
+    blocks on the device, and their bf16 expansion (the library's dequant)
+    for the many-token prompt."""
+    ht, tm, tables, layers, host = inputs
+    out = []
+    for l, (tab, _, qk) in enumerate(layers):
+        blocks = torch.from_numpy(G.wkv_q2k(w, l)).cuda()
+        wkv = torch.empty(w.N, w.K, dtype=torch.int16, device="cuda")
+        E.dequant_q2k(blocks, wkv)
+        out.append((tab, wkv, qk, blocks))
+    torch.cuda.synchronize()
+    return ht, tm, tables, out, host
+
+
+def decode_q2kw_bytes(w):
+    """Algorithmic bytes of one decode launch with wkv as Q2_K blocks: the
+    blocks (84 B per 256 weights) instead of the bf16 wkv, the rest as in
+    decode_bytes."""
+    return decode_bytes(w) - w.N * w.K * 2 + w.N * (w.K // 256) * 84
 
 
 def decode_bytes(w):
@@ -114,8 +139,8 @@ def decode_bytes(w):
             + 4 + 8 + 8 * w.max_ngram)
 
 
-def bench_decode(args, torch, E, G, synth, fused=True, inputs=None):
-    w = synth.DECODE_Q2K
+def bench_decode(args, torch, E, G, synth, fused=True, inputs=None, w=None):
+    w = synth.DECODE_Q2K if w is None else w
     if inputs is None:
         log(f"decode: generating {w.name}")
         inputs = device_inputs(w, torch, E, G)
@@ -164,7 +189,8 @@ def bench_decode(args, torch, E, G, synth, fused=True, inputs=None):
         ms_per_step=ms / args.steps,
         value=args.steps * nl / (ms / 1e3),
         proj_avg_ms=proj_ms / proj_n,
-        proj_bytes=decode_bytes(w) if fused else w.N * w.K * 2 + w.K * 2 + w.N * 2,
+        proj_bytes=(decode_q2kw_bytes(w) if w.wkv_fmt == "q2k" else decode_bytes(w)) if fused
+        else w.N * w.K * 2 + w.K * 2 + w.N * 2,
         stages={k: v[0] / max(1, v[1]) for k, v in stages.items() if v[1]},
         host=host, ht=ht, ids=ids,
     )
@@ -308,7 +334,13 @@ def main():
     staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=inputs)
     log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
         f"{staged['stages']}")
+    wq = synth.DECODE_WKVQ2K
+    qinputs = wkv_q2k_inputs(wq, inputs, torch, E, G)
     del inputs
+    decq = bench_decode(args, torch, E, G, synth, fused=True, inputs=qinputs, w=wq)
+    log(f"decode (Q2_K wkv): {decq['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
+        f"{decq['stages']}")
+    del qinputs
     pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
     if pre:
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
@@ -347,6 +379,15 @@ def main():
                           "gemv_GBps": staged_gbps, "gather_GBps": staged["gather_GBps"],
                           "gemv_traffic": counter_traffic("gemv_decode_counters.md",
                                                           "gemv.hip")},
+        "decode_wkv_q2k": {
+            "workload": wq.name, "ms_per_step": decq["ms_per_step"], "value": decq["value"],
+            "unit": "engram tokens/s per layer",
+            "stages_ms_per_layer_step": decq["stages"],
+            "kernel": "decode_q2kw_kernel<Q2K,6> (hash + gather/dequant + projection off the "
+                      "Q2_K wkv blocks; vector-ALU bound)",
+            "bytes_per_launch": decq["proj_bytes"], "avg_launch_ms": decq["proj_avg_ms"],
+            "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
+            "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3)},
         "prefill": pre,
         "cpu_baseline": cpu,
     }

@@ -119,13 +119,29 @@ __device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
     return acc;
 }
 
-// Sum over the 64 lanes of a wavefront; every lane gets the total.
+// v + (v of the lane that DPP control CTRL selects; 0 in rows outside ROWS).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront; every lane gets the total.  All in
+// VALU data-parallel moves (no LDS round trips): pairs and quads by quad
+// permutes, the 16-lane rows by half-row and row mirrors, then row 0 into
+// row 1 and row 2 into row 3 (row_bcast:15), rows 0..1 into row 3
+// (row_bcast:31), and lane 63's total read back as a uniform value.  The
+// order of the additions is fixed, so the sum is deterministic.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
+    v = dpp_add<0xB1, 0xF>(v);     // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);     // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);    // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);    // row_mirror
+    v = dpp_add<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // ------------------------------------------------------------------ host

@@ -56,9 +56,10 @@ struct DecodeArgs {
 };
 
 // Hash of the token and gather + dequant of this layer's cols rows into the
-// activations s_x (every workgroup; workgroup 0 also writes the row ids, the
-// history entry and the dequantised rows).  Ends with s_x complete.
-template <int FMT>
+// activations s_x by the NT threads of a workgroup (every workgroup;
+// workgroup 0 also writes the row ids, the history entry and the dequantised
+// rows).  Ends with s_x complete.
+template <int FMT, int NT>
 __device__ __forceinline__ void decode_prologue(const HashConsts &c, const DecodeArgs &a,
                                                 int64_t *s_id, uint32_t *s_blk, u32x4 *s_x)
 {
@@ -117,20 +118,20 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
 
     // ---- gather + dequant of the cols rows into the activations in LDS
     if (FMT == ENGRAM_FMT_Q2K) {
-        for (int i = tid; i < cols * 21; i += 256) {
+        for (int i = tid; i < cols * 21; i += NT) {
             const int r = i / 21, d = i - r * 21;
             const int64_t id = s_id[r];
             s_blk[i] = id >= 0 ? *(const uint32_t *)(a.table + id * ENGRAM_Q2K_ROW_BYTES + 4 * d)
                                : 0u;
         }
         __syncthreads();
-        for (int ch = tid; ch < kc; ch += 256) {
+        for (int ch = tid; ch < kc; ch += NT) {
             const int r = ch >> 5;
             s_x[ch] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
         }
     } else {
         const int nb = 256 / a.scale_block;
-        for (int ch = tid; ch < kc; ch += 256) {
+        for (int ch = tid; ch < kc; ch += NT) {
             const int r = ch >> 5, sub = ch & 31;
             const int64_t id = s_id[r];
             u32x4 o = zero;
@@ -143,7 +144,7 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
     }
     __syncthreads();
     if (blockIdx.x == 0)
-        for (int ch = tid; ch < kc; ch += 256)
+        for (int ch = tid; ch < kc; ch += NT)
             ((u32x4 *)a.rows)[ch] = s_x[ch];
 }
 
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
         }
     }
 
-    decode_prologue<FMT>(c, a, s_id, s_blk, s_x);
+    decode_prologue<FMT, 256>(c, a, s_id, s_blk, s_x);
 
     // ---- projection: rows wave, wave + n_waves, ...  A row's result is
     // stored after the next row's loads are issued, so the loop's wait for
@@ -205,16 +206,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
         y[prev_n] = prev_v;
 }
 
-// The same layer step with wkv as Q2_K blocks [N][K/256][84].
+// The same layer step with wkv as Q2_K blocks [N][K/256][84].  Here the
+// projection is bound by the vector ALUs, so the prologue's arithmetic
+// counts: one 1024-thread workgroup per CU runs it once for all sixteen
+// wavefronts of the CU.
+constexpr int kQ2kwThreads = 1024;
+
 template <int FMT, int NSB>
-__global__ __launch_bounds__(256) void decode_q2kw_kernel(const HashConsts c, const DecodeArgs a,
-                                                          const uint8_t *__restrict__ wq)
+__global__ __launch_bounds__(kQ2kwThreads) void decode_q2kw_kernel(const HashConsts c,
+                                                                   const DecodeArgs a,
+                                                                   const uint8_t *__restrict__ wq)
 {
     constexpr int NLD = q2k_row_loads<NSB>();
     __shared__ int64_t s_id[kDecodeMaxCols];
     __shared__ uint32_t s_blk[kDecodeMaxCols * 21];
     __shared__ u32x4 s_x[kMaxChunks];
-    __shared__ uint32_t s_row[4][kQ2kWkvMaxRowDwords];
+    __shared__ uint32_t s_row[kQ2kwThreads / 64][kQ2kWkvMaxRowDwords];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int K = c.cols * 256, n_sb = K >> 4, row_dwords = 21 * (K >> 8);
     const int64_t N = a.N;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_q2kw_kernel(const HashConsts c, co
     uint32_t r[NLD];
     q2k_row_load<NLD>(wd + min(wave, N - 1) * row_dwords, row_dwords, lane, r);
 
-    decode_prologue<FMT>(c, a, s_id, s_blk, s_x);
+    decode_prologue<FMT, kQ2kwThreads>(c, a, s_id, s_blk, s_x);
 
     // ---- this lane's sub-blocks of the activations, into registers
     uint32_t xr[NSB][8];
@@ -281,14 +288,18 @@ int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32
     const bool q2k_table = tab.fmt == ENGRAM_FMT_Q2K;
     if (w_q2k) {
         const int nsb = (int)((K + 1023) / 1024);
+        int64_t qblocks = (N + kQ2kwThreads / 64 - 1) / (kQ2kwThreads / 64);
+        if (qblocks > cus)
+            qblocks = cus;
+        const dim3 qgrid((unsigned)qblocks), qblock(kQ2kwThreads);
 #define ENGRAM_DECODE_Q2KW_CASE(S_)                                                              \
     case S_:                                                                                     \
         if (q2k_table)                                                                           \
-            dispatch(decode_q2kw_kernel<ENGRAM_FMT_Q2K, S_>, grid, block, l, true, true, c, a,   \
+            dispatch(decode_q2kw_kernel<ENGRAM_FMT_Q2K, S_>, qgrid, qblock, l, true, true, c, a, \
                      w_q2k);                                                                     \
         else                                                                                     \
-            dispatch(decode_q2kw_kernel<ENGRAM_FMT_E4M3, S_>, grid, block, l, true, true, c, a,  \
-                     w_q2k);                                                                     \
+            dispatch(decode_q2kw_kernel<ENGRAM_FMT_E4M3, S_>, qgrid, qblock, l, true, true, c,   \
+                     a, w_q2k);                                                                  \
         break;
         switch (nsb) {
             ENGRAM_DECODE_Q2KW_CASE(1) ENGRAM_DECODE_Q2KW_CASE(2) ENGRAM_DECODE_Q2KW_CASE(3)

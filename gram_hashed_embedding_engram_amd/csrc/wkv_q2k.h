@@ -14,13 +14,14 @@
 // A weight is bf16(d*scale*q - dmin*min) with q in 0..3 (the table rows'
 // decode, rounded the same way), so a sub-block has only four distinct
 // weights.  The lane computes those four (fma: exact product, one rounding,
-// then v_cvt_pk_bf16_f32's round to nearest even), spreads their low and
-// high bytes into two dwords, and turns every four 2-bit quants into two
-// bf16 weight pairs with byte permutes: the quants (one byte each after a
-// shift and mask) select the low byte and, offset by 4, the high byte.  Each
-// pair then meets its pair of activations in a v_dot2_f32_bf16.  About three
-// vector instructions a weight: the kernel is bound by the vector ALUs, not
-// by the 41 MB a layer it reads at the decode shape.
+// then v_cvt_pk_bf16_f32's round to nearest even) and spreads their low and
+// high bytes into two dwords.  Every four 2-bit quants, after a shift and a
+// mask one byte each, are then byte-permute selectors: one permute gathers
+// the four weights' low bytes, one their high bytes, and two more interleave
+// them into two bf16 weight pairs, each of which meets its pair of
+// activations in a v_dot2_f32_bf16.  About three vector instructions a
+// weight: the kernel is bound by the vector ALUs, not by the 41 MB a layer
+// it reads at the decode shape.
 #pragma once
 
 #include "common.h"
@@ -60,17 +61,19 @@ __device__ __forceinline__ void q2k_row_stage(uint32_t *lds, const uint32_t (&r)
 }
 
 // The row's dot product with the activations, this lane's share: sub-blocks
-// g = lane + 64*i < n_sb (n_sb = K/16); x[i][m] holds the bf16 pair of values
-// 16g+2m, 16g+2m+1.  lds = the row's blocks, 21 dwords each.
+// g = lane + 64*i < n_sb (n_sb = K/16, so only the last round, i = NSB-1,
+// can leave lanes idle); x[i][m] holds the bf16 pair of values 16g+2m,
+// 16g+2m+1.  lds = the row's blocks, 21 dwords each.  Two partial sums (the
+// first and second weight pair of every four) shorten the dependency chain.
 template <int NSB>
 __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const uint32_t (&x)[NSB][8],
                                              int n_sb, int lane)
 {
-    float acc = 0.0f;
+    float acc = 0.0f, acc2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < NSB; i++) {
         const int g = lane + 64 * i;
-        if (g >= n_sb)
+        if (i == NSB - 1 && g >= n_sb)
             break;
         const int b = g >> 4, sb = g & 15;
         const uint32_t *blk = lds + b * 21;
@@ -95,20 +98,19 @@ __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const uint32_t
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const uint32_t u = (q[j] >> shift) & 0x03030303u;     // quants of values 4j..4j+3
-            const uint32_t u4 = u | 0x04040404u;
-            const uint32_t s01 = __builtin_amdgcn_perm(u4, u, 0x05010400u);
-            const uint32_t s23 = __builtin_amdgcn_perm(u4, u, 0x07030602u);
-            const uint32_t wa = __builtin_amdgcn_perm(pool_hi, pool_lo, s01);
-            const uint32_t wb = __builtin_amdgcn_perm(pool_hi, pool_lo, s23);
+            const uint32_t lo = __builtin_amdgcn_perm(0u, pool_lo, u);   // low bytes of their weights
+            const uint32_t hi = __builtin_amdgcn_perm(0u, pool_hi, u);   // high bytes
+            const uint32_t wa = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // values 4j, 4j+1
+            const uint32_t wb = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // values 4j+2, 4j+3
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wa),
                                                   __builtin_bit_cast(bf16x2_t, x[i][2 * j]), acc,
                                                   false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wb),
-                                                  __builtin_bit_cast(bf16x2_t, x[i][2 * j + 1]),
-                                                  acc, false);
+            acc2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wb),
+                                                   __builtin_bit_cast(bf16x2_t, x[i][2 * j + 1]),
+                                                   acc2, false);
         }
     }
-    return acc;
+    return acc + acc2;
 }
 
 }  // namespace engram
