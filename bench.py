@@ -340,6 +340,9 @@ def main():
     decq = bench_decode(args, torch, E, G, synth, fused=True, inputs=qinputs, w=wq)
     log(f"decode (Q2_K wkv): {decq['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
         f"{decq['stages']}")
+    decq_staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=qinputs, w=wq)
+    log(f"decode (Q2_K wkv, staged): {decq_staged['ms_per_step'] * 1e3:.1f} us/step, "
+        f"stages(ms) {decq_staged['stages']}")
     del qinputs
     pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
     if pre:
@@ -387,7 +390,9 @@ def main():
                       "Q2_K wkv blocks; vector-ALU bound)",
             "bytes_per_launch": decq["proj_bytes"], "avg_launch_ms": decq["proj_avg_ms"],
             "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
-            "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3)},
+            "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
+            "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
+                       "stages_ms_per_layer_step": decq_staged["stages"]}},
         "prefill": pre,
         "cpu_baseline": cpu,
     }

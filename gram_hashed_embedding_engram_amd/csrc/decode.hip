@@ -208,12 +208,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
 
 // The same layer step with wkv as Q2_K blocks [N][K/256][84].  Here the
 // projection is bound by the vector ALUs, so the prologue's arithmetic
-// counts: one 1024-thread workgroup per CU runs it once for all sixteen
-// wavefronts of the CU.
+// counts: a 1024-thread workgroup runs it once for sixteen wavefronts, and
+// two workgroups share a CU (eight wavefronts a SIMD).
 constexpr int kQ2kwThreads = 1024;
+constexpr int kQ2kwBlocksPerCu = 2;
 
 template <int FMT, int NSB>
-__global__ __launch_bounds__(kQ2kwThreads) void decode_q2kw_kernel(const HashConsts c,
+__global__ __launch_bounds__(kQ2kwThreads, 8) void decode_q2kw_kernel(const HashConsts c,
                                                                    const DecodeArgs a,
                                                                    const uint8_t *__restrict__ wq)
 {
@@ -235,26 +236,12 @@ __global__ __launch_bounds__(kQ2kwThreads) void decode_q2kw_kernel(const HashCon
 
     decode_prologue<FMT, kQ2kwThreads>(c, a, s_id, s_blk, s_x);
 
-    // ---- this lane's sub-blocks of the activations, into registers
-    uint32_t xr[NSB][8];
-#pragma unroll
-    for (int i = 0; i < NSB; i++) {
-        const int g = lane + 64 * i;
-        u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
-        if (g < n_sb) {
-            lo = s_x[2 * g];
-            hi = s_x[2 * g + 1];
-        }
-        xr[i][0] = lo.x; xr[i][1] = lo.y; xr[i][2] = lo.z; xr[i][3] = lo.w;
-        xr[i][4] = hi.x; xr[i][5] = hi.y; xr[i][6] = hi.z; xr[i][7] = hi.w;
-    }
-
     // ---- projection, one row per wavefront at a time
     for (int64_t n = wave; n < N; n += n_waves) {
         q2k_row_stage<NLD>(s_row[wid], r, row_dwords, lane);
         if (n + n_waves < N)
             q2k_row_load<NLD>(wd + (n + n_waves) * row_dwords, row_dwords, lane, r);
-        const float s = wave_sum(q2k_row_dot<NSB>(s_row[wid], xr, n_sb, lane));
+        const float s = wave_sum(q2k_row_dot<NSB>(s_row[wid], s_x, n_sb, lane));
         if (lane == 0)
             a.y[n] = f32_to_bf16(s);
     }
@@ -289,8 +276,8 @@ int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32
     if (w_q2k) {
         const int nsb = (int)((K + 1023) / 1024);
         int64_t qblocks = (N + kQ2kwThreads / 64 - 1) / (kQ2kwThreads / 64);
-        if (qblocks > cus)
-            qblocks = cus;
+        if (qblocks > (int64_t)cus * kQ2kwBlocksPerCu)
+            qblocks = (int64_t)cus * kQ2kwBlocksPerCu;
         const dim3 qgrid((unsigned)qblocks), qblock(kQ2kwThreads);
 #define ENGRAM_DECODE_Q2KW_CASE(S_)                                                              \
     case S_:                                                                                     \

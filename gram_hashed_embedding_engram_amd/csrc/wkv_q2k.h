@@ -8,8 +8,9 @@
 // A wavefront handles one row at a time.  The row's 21*K/256 dwords arrive
 // as coalesced dword loads (the row is only 4-byte aligned) and are staged in
 // the wavefront's own LDS buffer; lane l then takes the row's 16-value
-// sub-blocks l, l+64, ..., with the token's activations for those sub-blocks
-// held in registers for the whole kernel.
+// sub-blocks l, l+64, ..., reading their activations from the token's copy in
+// LDS (registers stay few, so eight wavefronts fit on each SIMD to cover the
+// LDS and memory latencies).
 //
 // A weight is bf16(d*scale*q - dmin*min) with q in 0..3 (the table rows'
 // decode, rounded the same way), so a sub-block has only four distinct
@@ -62,18 +63,19 @@ __device__ __forceinline__ void q2k_row_stage(uint32_t *lds, const uint32_t (&r)
 
 // The row's dot product with the activations, this lane's share: sub-blocks
 // g = lane + 64*i < n_sb (n_sb = K/16, so only the last round, i = NSB-1,
-// can leave lanes idle); x[i][m] holds the bf16 pair of values 16g+2m,
-// 16g+2m+1.  lds = the row's blocks, 21 dwords each.  Two partial sums (the
-// first and second weight pair of every four) shorten the dependency chain.
+// can leave lanes idle).  xs = the token's activations in LDS as 8-value
+// chunks (chunks 2g, 2g+1 belong to sub-block g); lds = the row's blocks, 21
+// dwords each.  Two partial sums (the first and second weight pair of every
+// four) shorten the dependency chain.
 template <int NSB>
-__device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const uint32_t (&x)[NSB][8],
-                                             int n_sb, int lane)
+__device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const u32x4 *xs, int n_sb,
+                                             int lane)
 {
     float acc = 0.0f, acc2 = 0.0f;
-#pragma unroll
+#pragma unroll 1
     for (int i = 0; i < NSB; i++) {
         const int g = lane + 64 * i;
-        if (i == NSB - 1 && g >= n_sb)
+        if (g >= n_sb)
             break;
         const int b = g >> 4, sb = g & 15;
         const uint32_t *blk = lds + b * 21;
@@ -95,6 +97,8 @@ __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const uint32_t
         // bit 2*((sb>>1)&3) -- four dwords of quants, one shift
         const uint32_t *q = blk + 4 + 8 * (sb >> 3) + 4 * (sb & 1);
         const int shift = 2 * ((sb >> 1) & 3);
+        const u32x4 xa = xs[2 * g], xb = xs[2 * g + 1];
+        const uint32_t x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const uint32_t u = (q[j] >> shift) & 0x03030303u;     // quants of values 4j..4j+3
@@ -103,10 +107,10 @@ __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const uint32_t
             const uint32_t wa = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // values 4j, 4j+1
             const uint32_t wb = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // values 4j+2, 4j+3
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wa),
-                                                  __builtin_bit_cast(bf16x2_t, x[i][2 * j]), acc,
+                                                  __builtin_bit_cast(bf16x2_t, x[2 * j]), acc,
                                                   false);
             acc2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wb),
-                                                   __builtin_bit_cast(bf16x2_t, x[i][2 * j + 1]),
+                                                   __builtin_bit_cast(bf16x2_t, x[2 * j + 1]),
                                                    acc2, false);
         }
     }
