@@ -22,7 +22,8 @@ STAGES = ("hash", "gather", "project", "gate")
 
 # Every symbol include/engram.h declares.
 EXPORTS = (
-    "engram_last_error", "engram_abi_version", "engram_hash", "engram_gather_dequant",
+    "engram_last_error", "engram_abi_version", "engram_hash", "engram_hash_batch",
+    "engram_gather_dequant",
     "engram_project", "engram_project_q2k", "engram_dequant_q2k", "engram_qk_product",
     "engram_gate_apply", "engram_workspace_bytes",
     "engram_ctx_create", "engram_ctx_add_layer", "engram_ctx_set_wkv_q2k", "engram_reset",
@@ -56,7 +57,7 @@ class TableC(ctypes.Structure):
 
 class ConfigC(ctypes.Structure):
     _fields_ = [("hc", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dim", ctypes.c_int64),
-                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("batch", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("max_seq", ctypes.c_int64),
                 ("hash", HashTablesC)]
 
@@ -77,6 +78,7 @@ def lib():
             "engram_last_error": (ctypes.c_char_p, []),
             "engram_abi_version": (i32, []),
             "engram_hash": (i32, [p, p, i64, i64, p, i64, p, p, p]),
+            "engram_hash_batch": (i32, [p, p, i64, i64, i64, p, i64, p, p, p]),
             "engram_gather_dequant": (i32, [p, p, i64, i32, i64, p, p, p]),
             "engram_project": (i32, [p, p, p, i64, i64, i64, p]),
             "engram_project_q2k": (i32, [p, p, p, i64, i64, i64, p]),
@@ -168,6 +170,15 @@ def hash(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err=None,
                              _ptr(d_row_ids), _ptr(d_err), _stream(stream)))
 
 
+def hash_batch(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err=None,
+               stream=None):
+    """d_ids [B, T] int32, d_history [B, max_seq] int64, d_row_ids [B*T, nl, cols]."""
+    B, T = d_ids.shape
+    _check(lib().engram_hash_batch(ctypes.byref(tables.c), _ptr(d_ids), int(B), int(T),
+                                   int(start_pos), _ptr(d_history), int(d_history.shape[1]),
+                                   _ptr(d_row_ids), _ptr(d_err), _stream(stream)))
+
+
 def gather_dequant(table: Table, d_row_ids, T, cols, id_stride, d_rows, d_err=None,
                    stream=None):
     _check(lib().engram_gather_dequant(ctypes.byref(table.c), _ptr(d_row_ids), int(T),
@@ -209,10 +220,11 @@ class Context:
     """The stateful engram of one sequence (engram_ctx)."""
 
     def __init__(self, tables: HashTables, hc, dim, head_dim, eps, max_tokens, max_seq,
-                 d_workspace=None):
+                 d_workspace=None, batch=1):
         import torch
         self.tables = tables
-        self.cfg = ConfigC(hc, head_dim, dim, eps, 0, max_tokens, max_seq, tables.c)
+        self.batch = batch
+        self.cfg = ConfigC(hc, head_dim, dim, eps, batch, max_tokens, max_seq, tables.c)
         nbytes = lib().engram_workspace_bytes(ctypes.byref(self.cfg))
         if nbytes == 0:
             raise EngramError(E_ARG, "invalid engram configuration")
@@ -259,8 +271,9 @@ class Context:
         return tuple(q.value for q in ptrs)
 
     def views(self, T):
-        """torch views of the workspace: row ids [T, nl, cols] int64, rows
-        [T, cols*head_dim] bf16 bits (int16), kv [T, dim*(hc+1)] (int16)."""
+        """torch views of the workspace for a call of T tokens a sequence
+        (M = batch*T): row ids [M, nl, cols] int64, rows [M, cols*head_dim]
+        bf16 bits (int16), kv [M, dim*(hc+1)] (int16)."""
         import torch
         ws = self.workspace
         base = ws.data_ptr()
@@ -272,9 +285,10 @@ class Context:
             return ws[off:off + n * size].view(dtype).view(*shape)
 
         K, N = self.cols * self.head_dim, self.dim * (self.hc + 1)
-        return (view(rid, T * self.nl * self.cols, torch.int64, (T, self.nl, self.cols)),
-                view(rows, T * K, torch.int16, (T, K)),
-                view(kv, T * N, torch.int16, (T, N)))
+        M = self.batch * T
+        return (view(rid, M * self.nl * self.cols, torch.int64, (M, self.nl, self.cols)),
+                view(rows, M * K, torch.int16, (M, K)),
+                view(kv, M * N, torch.int16, (M, N)))
 
     def set_fused_decode(self, on: bool):
         _check(lib().engram_ctx_set_fused_decode(self.h, 1 if on else 0))

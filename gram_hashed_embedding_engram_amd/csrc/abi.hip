@@ -45,6 +45,7 @@ namespace {
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
+constexpr int32_t kMaxBatch = 4096;         // sequences per context
 
 // Hash tables -> kernel constants (atlascybernetics "engram_v41.rs",
 // EngramHashTables::from_flat: geometry and array checks).
@@ -233,22 +234,26 @@ struct Carve {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// sequences of a context (0 in the config means one)
+int64_t batch_of(const engram_config *cfg) { return cfg->batch > 0 ? cfg->batch : 1; }
+
 bool carve(const engram_config *cfg, Carve *c)
 {
     if (!cfg || cfg->max_tokens <= 0 || cfg->max_seq <= 0 || cfg->dim <= 0 || cfg->hc <= 0 ||
         cfg->head_dim <= 0 || cfg->hash.n_layers <= 0 || cfg->hash.max_ngram < 2 ||
-        cfg->hash.n_heads <= 0)
+        cfg->hash.n_heads <= 0 || cfg->batch < 0 || cfg->batch > kMaxBatch)
         return false;
     const int64_t cols = (int64_t)(cfg->hash.max_ngram - 1) * cfg->hash.n_heads;
+    const int64_t B = batch_of(cfg), M = B * cfg->max_tokens;
     size_t off = 0;
     c->history = off;
-    off += round256(sizeof(int64_t) * (size_t)cfg->max_seq);
+    off += round256(sizeof(int64_t) * (size_t)(B * cfg->max_seq));
     c->row_ids = off;
-    off += round256(sizeof(int64_t) * (size_t)(cfg->max_tokens * cfg->hash.n_layers * cols));
+    off += round256(sizeof(int64_t) * (size_t)(M * cfg->hash.n_layers * cols));
     c->rows = off;
-    off += round256(2 * (size_t)(cfg->max_tokens * cols * cfg->head_dim));
+    off += round256(2 * (size_t)(M * cols * cfg->head_dim));
     c->kv = off;
-    off += round256(2 * (size_t)(cfg->max_tokens * cfg->dim * (cfg->hc + 1)));
+    off += round256(2 * (size_t)(M * cfg->dim * (cfg->hc + 1)));
     c->err = off;
     off += 256;
     c->total = off;
@@ -303,24 +308,34 @@ const char *engram_last_error(void) { return g_last_error.c_str(); }
 
 int32_t engram_abi_version(void) { return ENGRAM_ABI_VERSION; }
 
-int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int64_t T,
-                    int64_t start_pos, int64_t *d_history, int64_t max_seq, int64_t *d_row_ids,
-                    int32_t *d_err, void *stream)
+int32_t engram_hash_batch(const engram_hash_tables *tables, const int32_t *d_ids, int64_t B,
+                          int64_t T, int64_t start_pos, int64_t *d_history, int64_t max_seq,
+                          int64_t *d_row_ids, int32_t *d_err, void *stream)
 {
     HashConsts c;
     int32_t rc = make_consts(tables, &c);
     if (rc != ENGRAM_OK)
         return rc;
-    CHECK(T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
-          "engram hash: T %lld, start_pos %lld, max_seq %lld", (long long)T,
-          (long long)start_pos, (long long)max_seq);
+    CHECK(B >= 0 && T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
+          "engram hash: B %lld, T %lld, start_pos %lld, max_seq %lld", (long long)B,
+          (long long)T, (long long)start_pos, (long long)max_seq);
     CHECK(start_pos + T <= max_seq, ENGRAM_E_RANGE, "engram hasher: %lld positions, %lld needed",
           (long long)max_seq, (long long)(start_pos + T));
-    if (T == 0)
+    CHECK(B == 0 || T == 0 || B <= ((int64_t)1 << 40) / T, ENGRAM_E_RANGE,
+          "engram hash: %lld x %lld tokens", (long long)B, (long long)T);
+    if (B == 0 || T == 0)
         return ENGRAM_OK;
     CHECK(d_ids && d_history && d_row_ids, ENGRAM_E_ARG, "engram hash: NULL pointer");
-    return launch_hash(c, tables->d_token_map, d_ids, T, start_pos, d_history, d_row_ids, d_err,
-                       on(stream));
+    return launch_hash(c, tables->d_token_map, d_ids, B, T, start_pos, d_history, max_seq,
+                       d_row_ids, d_err, on(stream));
+}
+
+int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int64_t T,
+                    int64_t start_pos, int64_t *d_history, int64_t max_seq, int64_t *d_row_ids,
+                    int32_t *d_err, void *stream)
+{
+    return engram_hash_batch(tables, d_ids, 1, T, start_pos, d_history, max_seq, d_row_ids, d_err,
+                             stream);
 }
 
 int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_ids, int64_t T,
@@ -414,13 +429,16 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
           ENGRAM_E_UNSUPPORTED, "engram head_dim %d", cfg->head_dim);
     CHECK(std::isfinite(cfg->eps) && cfg->eps >= 0.0f, ENGRAM_E_ARG, "engram eps %g",
           (double)cfg->eps);
+    CHECK(cfg->batch >= 0 && cfg->batch <= kMaxBatch, ENGRAM_E_ARG,
+          "engram ctx: batch %d outside 0..%d", cfg->batch, kMaxBatch);
     CHECK(cfg->max_tokens >= 1 && cfg->max_seq >= 1, ENGRAM_E_ARG,
           "engram ctx: max_tokens %lld, max_seq %lld", (long long)cfg->max_tokens,
           (long long)cfg->max_seq);
     const int64_t K = (int64_t)c.cols * cfg->head_dim, N = cfg->dim * (cfg->hc + 1);
     CHECK(K % 64 == 0, ENGRAM_E_UNSUPPORTED, "engram ctx: cols*head_dim = %lld not a multiple of 64",
           (long long)K);
-    CHECK((cfg->max_tokens + 256) * K < kMaxElems && (N + 256) * K < kMaxElems, ENGRAM_E_UNSUPPORTED,
+    CHECK((batch_of(cfg) * cfg->max_tokens + 256) * K < kMaxElems && (N + 256) * K < kMaxElems,
+          ENGRAM_E_UNSUPPORTED,
           "engram ctx: projection operands exceed 2^31 elements");
     Carve cv;
     carve(cfg, &cv);
@@ -498,7 +516,8 @@ int32_t engram_reset(engram_ctx *ctx, void *stream)
 {
     CHECK(ctx, ENGRAM_E_ARG, "engram reset: NULL context");
     const Launch l = on(stream);
-    int32_t rc = launch_fill_zero(ctx->history, sizeof(int64_t) * (size_t)ctx->cfg.max_seq, l);
+    int32_t rc = launch_fill_zero(
+        ctx->history, sizeof(int64_t) * (size_t)(batch_of(&ctx->cfg) * ctx->cfg.max_seq), l);
     if (rc == ENGRAM_OK)
         rc = launch_fill_zero(ctx->err, 256, l);
     if (rc != ENGRAM_OK)
@@ -537,9 +556,10 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     CHECK(ctx->was_reset, ENGRAM_E_STATE, "engram forward: the context needs engram_reset first");
     hipStream_t s = as_stream(stream);
     const engram_config &cfg = ctx->cfg;
+    const int64_t B = batch_of(&cfg), M = B * T;   // tokens of the call, sequence-major
     int32_t rc;
-    // one decode token: hash, gather and projection in one launch
-    if (T == 1 && ctx->fused_decode && cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols) {
+    // one decode token of one sequence: hash, gather and projection in one launch
+    if (M == 1 && ctx->fused_decode && cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols) {
         if (hash_index == 0) {
             ctx->step_start = ctx->pos;
             ctx->pos += 1;
@@ -561,8 +581,8 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     if (hash_index == 0) {
         const int64_t start = ctx->pos;
         rc = staged(ctx, 0, s, [&](const Launch &l) {
-            return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, T, start, ctx->history,
-                               ctx->row_ids, ctx->err, l);
+            return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, B, T, start,
+                               ctx->history, cfg.max_seq, ctx->row_ids, ctx->err, l);
         });
         if (rc != ENGRAM_OK)
             return rc;
@@ -573,20 +593,20 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     }
     const int64_t K = (int64_t)ctx->cols * cfg.head_dim;
     rc = staged(ctx, 1, s, [&](const Launch &l) {
-        return launch_gather(L.tab, ctx->row_ids + (int64_t)hash_index * ctx->cols, T, ctx->cols,
+        return launch_gather(L.tab, ctx->row_ids + (int64_t)hash_index * ctx->cols, M, ctx->cols,
                              (int64_t)ctx->nl * ctx->cols, ctx->rows, ctx->err, l);
     });
     if (rc != ENGRAM_OK)
         return rc;
     rc = staged(ctx, 2, s, [&](const Launch &l) {
-        if (T == 1 && L.wkv_q2k)
+        if (M == 1 && L.wkv_q2k)
             return launch_gemv_q2k(ctx->rows, L.wkv_q2k, ctx->kv, K, ctx->kv_width, l);
-        return dispatch_project(ctx->rows, L.wkv, ctx->kv, T, K, ctx->kv_width, l);
+        return dispatch_project(ctx->rows, L.wkv, ctx->kv, M, K, ctx->kv_width, l);
     });
     if (rc != ENGRAM_OK)
         return rc;
     return staged(ctx, 3, s, [&](const Launch &l) {
-        return launch_gate(d_h, ctx->kv, L.qk, T, cfg.hc, cfg.dim, cfg.eps, l);
+        return launch_gate(d_h, ctx->kv, L.qk, M, cfg.hc, cfg.dim, cfg.eps, l);
     });
 }
 

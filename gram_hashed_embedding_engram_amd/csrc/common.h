@@ -182,9 +182,11 @@ struct HashConsts {
 
 // Launchers (each in its kernel's source file).  Arguments are validated by
 // the caller; these only enqueue.
-int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t T,
-                    int64_t start_pos, int64_t *history, int64_t *row_ids, int32_t *err,
-                    const Launch &l);
+// B sequences of T tokens at position start_pos: ids [B][T], history
+// [B][hist_stride], row_ids [B*T][n_layers][cols].
+int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t B,
+                    int64_t T, int64_t start_pos, int64_t *history, int64_t hist_stride,
+                    int64_t *row_ids, int32_t *err, const Launch &l);
 int32_t launch_gather(const engram_table &tab, const int64_t *row_ids, int64_t T, int32_t cols,
                       int64_t id_stride, uint16_t *rows, int32_t *err, const Launch &l);
 int32_t launch_gemv(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T, int64_t K,

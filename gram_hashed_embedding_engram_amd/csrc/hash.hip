@@ -2,12 +2,14 @@
 // EngramHasher::hash; metrale "deepseek_v41_ref/engram.rs",
 // NgramHashState::forward), data-parallel on the GPU.
 //
-// One thread per (token, layer, head).  Each thread rebuilds its token's
-// window of compressed ids: a position inside this call is read through the
-// token map from the call's own ids, a position before it from the history
-// buffer, so no thread reads a history entry another thread of the same
-// launch writes.  The first thread of each token records the token's
-// compressed id in the history for later calls.
+// One thread per (sequence, token, layer, head) for B sequences at one
+// common position (NgramHashState's batch rows, each with its own cache).
+// Each thread rebuilds its token's window of compressed ids: a position
+// inside this call is read through the token map from the call's own ids, a
+// position before it from its sequence's history row, so no thread reads a
+// history entry another thread of the same launch writes.  The first thread
+// of each token records the token's compressed id in the history for later
+// calls.
 //
 // Arithmetic: the window hash is kept in uint64 (wrapping multiply and XOR
 // are the two's-complement i64 operations of the pages); the remainder is
@@ -19,19 +21,23 @@ namespace {
 
 __global__ __launch_bounds__(256) void hash_kernel(const HashConsts c,
                                                    const int64_t *__restrict__ token_map,
-                                                   const int32_t *__restrict__ ids, int64_t T,
-                                                   int64_t start_pos,
-                                                   int64_t *__restrict__ history,
+                                                   const int32_t *__restrict__ ids_all, int64_t B,
+                                                   int64_t T, int64_t start_pos,
+                                                   int64_t *__restrict__ history_all,
+                                                   int64_t hist_stride,
                                                    int64_t *__restrict__ row_ids,
                                                    int32_t *__restrict__ err)
 {
     const int64_t per_token = (int64_t)c.nl * c.nh;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= T * per_token)
+    if (gid >= B * T * per_token)
         return;
-    const int64_t j = gid / per_token;
-    const int r = (int)(gid - j * per_token);
+    const int64_t bt = gid / per_token;              // token b*T + j of the call
+    const int r = (int)(gid - bt * per_token);
     const int l = r / c.nh, head = r - l * c.nh;
+    const int64_t b = bt / T, j = bt - b * T;
+    const int32_t *ids = ids_all + b * T;
+    int64_t *history = history_all + b * hist_stride;
     const int64_t pos = start_pos + j;
 
     // the window, newest first, with the sticky pad rule
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashConsts c,
 
     const int64_t *m = c.mult + l * c.ng;
     uint64_t rolling = (uint64_t)tok[0] * (uint64_t)m[0];
-    int64_t *out = row_ids + (j * c.nl + l) * c.cols;
+    int64_t *out = row_ids + (bt * c.nl + l) * c.cols;
 #pragma unroll
     for (int i = 1; i < ENGRAM_MAX_NGRAM; i++) {
         if (i < c.ng) {
@@ -88,16 +94,16 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashConsts c,
 
 }  // namespace
 
-int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t T,
-                    int64_t start_pos, int64_t *history, int64_t *row_ids, int32_t *err,
-                    const Launch &l)
+int32_t launch_hash(const HashConsts &c, const int64_t *token_map, const int32_t *ids, int64_t B,
+                    int64_t T, int64_t start_pos, int64_t *history, int64_t hist_stride,
+                    int64_t *row_ids, int32_t *err, const Launch &l)
 {
-    const int64_t threads = T * c.nl * c.nh;
+    const int64_t threads = B * T * c.nl * c.nh;
     if (threads == 0)
         return ENGRAM_OK;
     const int64_t blocks = (threads + 255) / 256;
-    dispatch(hash_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, c, token_map, ids, T,
-             start_pos, history, row_ids, err);
+    dispatch(hash_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, c, token_map, ids, B,
+             T, start_pos, history, hist_stride, row_ids, err);
     return launch_status("engram hash kernel");
 }
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_ABI_VERSION 2
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -112,6 +112,16 @@ typedef struct engram_hash_tables {
 int32_t engram_hash(const engram_hash_tables *tables, const int32_t *d_ids, int64_t T,
                     int64_t start_pos, int64_t *d_history, int64_t max_seq,
                     int64_t *d_row_ids, int32_t *d_err, void *stream);
+
+/* The same hash for B sequences at one common position, each with its own
+ * cache (metrale "engram.rs", NgramHashState: input_ids [batch, seqlen],
+ * cache [batch * max_seq], output [batch, seqlen, n_layers, n_hash_cols]):
+ *   d_ids [B][T] int32, d_history [B][max_seq] int64 (row b is sequence b's
+ *   cache, as in engram_hash), d_row_ids [B*T][n_layers][cols] int64.
+ * B = 1 is engram_hash.  B = 0 or T = 0 is a no-op. */
+int32_t engram_hash_batch(const engram_hash_tables *tables, const int32_t *d_ids, int64_t B,
+                          int64_t T, int64_t start_pos, int64_t *d_history, int64_t max_seq,
+                          int64_t *d_row_ids, int32_t *d_err, void *stream);
 
 /* -------------------------------------------------------- gather + dequant */
 
@@ -207,24 +217,27 @@ int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, i
 
 /* --------------------------------------------------- stateful engram layer */
 
-/* One sequence's engram: hash tables, up to n_layers registered layers and a
- * caller-owned workspace holding the hasher history, the step's row ids, the
- * dequantised rows, the projection output and the device error word
- * (atlascybernetics "engram_v41.rs", EngramV41 and EngramHasher;
- * "deepseek_v41_layer.rs", V41Runtime::step_hashes).  One context serves one
- * sequence; calls on one context must not overlap. */
+/* The engram of one sequence, or of `batch` sequences that advance together
+ * (metrale "engram.rs", NgramHashState's batch rows): hash tables, up to
+ * n_layers registered layers and a caller-owned workspace holding the hasher
+ * history of every sequence, the step's row ids, the dequantised rows, the
+ * projection output and the device error word (atlascybernetics
+ * "engram_v41.rs", EngramV41 and EngramHasher; "deepseek_v41_layer.rs",
+ * V41Runtime::step_hashes).  A step's tokens of all sequences go through one
+ * pass over each layer's weights.  Calls on one context must not overlap. */
 typedef struct engram_ctx engram_ctx;
 
 /* Geometry: hc in 1..4; dim a multiple of 256; head_dim of every layer's
- * table; eps of the gate; max_tokens per call; max_seq positions of history.
- * hash.multipliers/primes/offsets are copied at create. */
+ * table; eps of the gate; batch sequences (0 or 1: one; up to 4096);
+ * max_tokens per sequence per call; max_seq positions of history per
+ * sequence.  hash.multipliers/primes/offsets are copied at create. */
 typedef struct engram_config {
     int32_t hc;
     int32_t head_dim;
     int64_t dim;
     float eps;
-    int32_t reserved;
-    int64_t max_tokens;
+    int32_t batch;          /* sequences (0 = 1); they advance together */
+    int64_t max_tokens;     /* tokens per sequence per call */
     int64_t max_seq;
     engram_hash_tables hash;
 } engram_config;
@@ -258,11 +271,11 @@ int32_t engram_ctx_set_wkv_q2k(engram_ctx *ctx, int32_t hash_index, const uint8_
 /* History := 0, position := 0, device error word := 0, no step open. */
 int32_t engram_reset(engram_ctx *ctx, void *stream);
 
-/* One engram layer over the next T tokens of the sequence, gating d_h
- * [T][hc][dim] in place.  hash_index 0 opens a step: it hashes the T tokens
- * d_ids [T] for every layer at the current position and advances the
- * position by T (the look-back carries across prefill chunks and decode
- * steps).  hash_index > 0 reuses the open step's row ids (d_ids is ignored
+/* One engram layer over the next T tokens of every sequence, gating d_h
+ * [batch][T][hc][dim] in place.  hash_index 0 opens a step: it hashes the
+ * tokens d_ids [batch][T] (sequence b's in row b, against its own history)
+ * for every layer at the current position and advances the position by T
+ * (the look-back carries across prefill chunks and decode steps).  hash_index > 0 reuses the open step's row ids (d_ids is ignored
  * and may be NULL) and must pass the same T (atlascybernetics
  * "deepseek_v41_layer.rs", V41Runtime::step_hashes: computed by the first
  * engram layer, reused by the second).
@@ -282,12 +295,14 @@ int32_t engram_check(engram_ctx *ctx, void *stream);
 int64_t engram_position(const engram_ctx *ctx);
 
 /* Device views into the workspace (any output may be NULL): the open step's
- * row ids [T][n_layers][cols] int64, the last forward's rows [T][cols*head_dim]
- * bf16 and kv [T][dim*(hc+1)] bf16.  Valid until the next forward. */
+ * row ids [batch*T][n_layers][cols] int64, the last forward's rows
+ * [batch*T][cols*head_dim] bf16 and kv [batch*T][dim*(hc+1)] bf16 (token b*T+t
+ * is token t of sequence b).  Valid until the next forward. */
 int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t **d_rows,
                            uint16_t **d_kv, int32_t **d_err);
 
-/* One decode token (T = 1, head_dim 256, at most 32 columns) runs hash,
+/* One decode token of a one-sequence context (T = 1, head_dim 256, at most
+ * 32 columns) runs hash,
  * gather + dequant and the projection of a layer as one kernel, then the gate
  * (enabled by default).  Results and workspace contents (row ids of every
  * layer, rows, kv, history, highway) are bit-identical to the staged path's.

@@ -80,10 +80,11 @@ class Device:
             self.qk.append(qk)
         torch.cuda.synchronize()
 
-    def context(self, max_tokens, max_seq):
+    def context(self, max_tokens, max_seq, batch=1):
         import gram_hashed_embedding_engram_amd as E
         w = self.w
-        ctx = E.Context(self.tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
+        ctx = E.Context(self.tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq,
+                        batch=batch)
         for l in range(w.n_layers):
             ctx.add_layer(l, self.tab[l], self.wkv[l], self.qk[l])
             if self.wkvq[l] is not None:

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 1
+    assert L.engram_abi_version() == 2
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
@@ -86,6 +86,13 @@ def test_hash_refusals(L):
     # NULL pointers
     assert L.engram_hash(ctypes.byref(c), None, 4, 0, FAKE, 16, FAKE, None, None) == E.E_ARG
     assert L.engram_hash(None, FAKE, 4, 0, FAKE, 16, FAKE, None, None) == E.E_ARG
+    # the batched form: same checks, B = 0 or T = 0 launch nothing
+    hb = lambda B, T=4, start=0, max_seq=16, ids=FAKE: L.engram_hash_batch(
+        ctypes.byref(c), ids, B, T, start, FAKE, max_seq, FAKE, None, None)
+    assert hb(-1) == E.E_ARG
+    assert hb(3, T=10, start=8) == E.E_RANGE
+    assert hb(3, ids=None) == E.E_ARG
+    assert hb(0, ids=None) == E.OK and hb(3, T=0, ids=None) == E.OK
 
 
 def test_gather_refusals(L):
@@ -151,9 +158,9 @@ def test_gate_refusals(L):
     assert L.engram_qk_product(FAKE, FAKE, FAKE, 0, None) == E.OK
 
 
-def make_cfg(max_tokens=64, max_seq=512, hc=4, dim=4096, head_dim=256, tables=None):
+def make_cfg(max_tokens=64, max_seq=512, hc=4, dim=4096, head_dim=256, tables=None, batch=0):
     c, keep = tables or tables_c()
-    cfg = E.ConfigC(hc, head_dim, dim, 1e-6, 0, max_tokens, max_seq, c)
+    cfg = E.ConfigC(hc, head_dim, dim, 1e-6, batch, max_tokens, max_seq, c)
     return cfg, keep
 
 
@@ -166,6 +173,16 @@ def test_workspace_layout(L):
     assert n == want
     bad, _ = make_cfg(max_tokens=0)
     assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0
+    # batch sequences: a history row each, batch*max_tokens tokens of buffers
+    one, _ = make_cfg(batch=1)
+    assert L.engram_workspace_bytes(ctypes.byref(one)) == want
+    b3, _ = make_cfg(batch=3)
+    assert L.engram_workspace_bytes(ctypes.byref(b3)) == (
+        r256(8 * 512 * 3) + r256(8 * 192 * 2 * 24) + r256(2 * 192 * 24 * 256)
+        + r256(2 * 192 * 4096 * 5) + 256)
+    for bad_batch in (-1, 4097):
+        bad, _ = make_cfg(batch=bad_batch)
+        assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0
 
 
 def test_context_refusals_and_state(L):

@@ -37,9 +37,10 @@ def cuda(a):
 
 def check_call(dev, ctx, layer, ids_np, hasher_out, h_before, h_after, T, sample_tokens=None,
                sample_cols=None, label=""):
-    """Compare one forward call's intermediates and output with the oracle."""
+    """Compare one forward call's intermediates and output with the oracle
+    (T = all tokens of the call, batch * tokens per sequence)."""
     w = dev.w
-    rid, rows, kv = ctx.views(T)
+    rid, rows, kv = ctx.views(T // ctx.batch)
     rid = rid.cpu().numpy()
     np.testing.assert_array_equal(rid, hasher_out, err_msg=f"{label} hash ids")
     rows = to_np_u16(rows)
@@ -146,6 +147,41 @@ def test_forward_decode_wkv_q2k(E):
                                       label=f"step {step} layer {layer}")
             worst = [max(worst[0], e_kv), max(worst[1], e_h)]
         pos += T
+    ctx.check()
+    log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("B,prompt,steps", [(4, 8, 16), (6, 4, 4)])
+def test_forward_batched_sequences(E, B, prompt, steps):
+    """B sequences decoded together (one token of each per step through one
+    pass over each layer's weights): every token's ids, rows, kv and highway
+    against the oracle run on that sequence alone.  B = 4 single-token steps
+    take the GEMV, B = 6 the GEMM."""
+    w = synth.DECODE_Q2K
+    log(f"forward: {B} sequences, prompt {prompt} + {steps} steps, 2 layers")
+    dev = Device(w.name)
+    rng = np.random.default_rng(B)
+    n = prompt + steps
+    ids = rng.integers(0, w.vocab, size=(B, n)).astype(np.int32)
+    ctx = dev.context(max_tokens=prompt, max_seq=n, batch=B)
+    hashers = [dev.oracle_hasher(n) for _ in range(B)]
+    h_all = rng.standard_normal((B, n, w.hc, w.dim)).astype(np.float32)
+    pos = 0
+    worst = [0.0, 0.0]
+    for step in range(1 + steps):
+        T = prompt if step == 0 else 1
+        want_ids = np.concatenate([hashers[b].hash(ids[b, pos:pos + T], pos) for b in range(B)])
+        h0 = np.ascontiguousarray(h_all[:, pos:pos + T]).reshape(B * T, w.hc, w.dim)
+        d_ids = cuda(np.ascontiguousarray(ids[:, pos:pos + T]))
+        for layer in range(2):
+            d_h = torch.from_numpy(h0).cuda()
+            ctx.forward(layer, d_ids if layer == 0 else None, T, d_h)
+            h1 = d_h.cpu().numpy()
+            e_kv, e_h, _ = check_call(dev, ctx, layer, None, want_ids, h0, h1, B * T,
+                                      label=f"B={B} step {step} layer {layer}")
+            worst = [max(worst[0], e_kv), max(worst[1], e_h)]
+        pos += T
+        assert ctx.position == pos
     ctx.check()
     log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
 

@@ -50,6 +50,30 @@ def cuda(a):
 
 
 # ------------------------------------------------------------------ hash
+def test_hash_batch_matches_per_sequence_oracle(E, decode):
+    """B sequences hashed together, each against its own history row, over two
+    calls (look-back across the calls), equal the oracle hasher run on each
+    sequence alone."""
+    w = decode.w
+    B, T0, T1, max_seq = 5, 6, 3, 16
+    rng = np.random.default_rng(17)
+    ids = rng.integers(0, w.vocab, size=(B, T0 + T1)).astype(np.int32)
+    ids[2, 4] = int(np.nonzero(decode.ht["token_map"] == -1)[0][0])    # an unmapped token
+    hist = torch.zeros(B, max_seq, dtype=torch.int64, device="cuda")
+    got = []
+    for start, T in ((0, T0), (T0, T1)):
+        out = torch.empty(B * T, w.n_layers, w.cols, dtype=torch.int64, device="cuda")
+        E.hash_batch(decode.tables, cuda(ids[:, start:start + T]), start, hist, out)
+        got.append(out.cpu().numpy().reshape(B, T, w.n_layers, w.cols))
+    log(f"hash batch: B={B}, calls of {T0} and {T1} tokens")
+    for b in range(B):
+        h = decode.oracle_hasher(max_seq)
+        want0 = h.hash(ids[b, :T0], 0)
+        want1 = h.hash(ids[b, T0:], T0)
+        np.testing.assert_array_equal(got[0][b], want0, err_msg=f"sequence {b} call 0")
+        np.testing.assert_array_equal(got[1][b], want1, err_msg=f"sequence {b} call 1")
+
+
 def run_hash(E, dev, ids, start, hist):
     T = ids.size
     out = torch.empty(T, dev.w.n_layers, dev.w.cols, dtype=torch.int64, device="cuda")
