@@ -97,8 +97,8 @@ def device_inputs(w, torch, E, G):
     return ht, tm, tables, layers, host
 
 
-def make_ctx(E, w, tables, layers, max_tokens, max_seq):
-    ctx = E.Context(tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq)
+def make_ctx(E, w, tables, layers, max_tokens, max_seq, batch=1):
+    ctx = E.Context(tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq, batch=batch)
     for l, layer in enumerate(layers):
         tab, wkv, qk = layer[:3]
         ctx.add_layer(l, tab, wkv, qk)
@@ -201,6 +201,57 @@ def bench_decode(args, torch, E, G, synth, fused=True, inputs=None, w=None):
     return res
 
 
+def bench_decode_batched(args, torch, E, G, synth, inputs, B):
+    """B sequences decoded together on the decode workload's tables and
+    weights: a prompt of w.prompt tokens each, then single-token steps, every
+    step one pass over each layer's weights for B tokens.  Token ids: the
+    decode workload's stream cut into B sequences."""
+    w = synth.DECODE_Q2K
+    ht, tm, tables, layers, host = inputs
+    n_tok = w.prompt + 2 * (args.warmup + args.steps)
+    ids = G.token_ids(w, n_tok * B).reshape(B, n_tok)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    hw = torch.from_numpy(G.highway(w, w.decode_steps, decode=True)).cuda()
+    prompt_h = torch.from_numpy(G.highway(w, B * w.prompt)).cuda()
+    ctx = make_ctx(E, w, tables, layers, w.prompt, n_tok, batch=B)
+    stream = torch.cuda.current_stream()
+    nl = w.n_layers
+    for l in range(nl):
+        ctx.forward(l, d_ids[:, :w.prompt].contiguous(), w.prompt, prompt_h)
+    pos = w.prompt
+    steps_h = [hw[(i * B) % (w.decode_steps - B):(i * B) % (w.decode_steps - B) + B]
+               for i in range(max(args.steps, args.warmup))]
+    step_ids = [d_ids[:, p:p + 1].contiguous() for p in range(n_tok)]
+
+    def step(i):
+        nonlocal pos
+        for l in range(nl):
+            ctx.forward(l, step_ids[pos], 1, steps_h[i])
+        pos += 1
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ctx.set_timing(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = ctx.timing()
+    ctx.check()
+    del ctx
+    return dict(sequences=B, ms_per_step=ms / args.steps,
+                value=args.steps * B * nl / (ms / 1e3), unit="engram tokens/s per layer",
+                stages_ms_per_layer_step={k: v[0] / max(1, v[1]) for k, v in stages.items()
+                                          if v[1]})
+
+
 def bench_prefill(args, torch, E, G, synth):
     w = synth.PREFILL_Q2K
     log(f"prefill: generating {w.name}")
@@ -294,6 +345,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--batch-sequences", type=int, nargs="*", default=[4],
+                    help="also decode this many sequences together (one weight pass per step)")
     ap.add_argument("--no-decode", action="store_true",
                     help="run only the prefill measurement (for counter passes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -334,6 +387,12 @@ def main():
     staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=inputs)
     log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
         f"{staged['stages']}")
+    batched = []
+    for B in args.batch_sequences:
+        r = bench_decode_batched(args, torch, E, G, synth, inputs, B)
+        log(f"decode ({B} sequences): {r['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{r['value']:.0f} tokens/s per layer, stages(ms) {r['stages_ms_per_layer_step']}")
+        batched.append(r)
     wq = synth.DECODE_WKVQ2K
     qinputs = wkv_q2k_inputs(wq, inputs, torch, E, G)
     del inputs
@@ -393,6 +452,7 @@ def main():
             "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
             "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
                        "stages_ms_per_layer_step": decq_staged["stages"]}},
+        "decode_batched": batched,
         "prefill": pre,
         "cpu_baseline": cpu,
     }

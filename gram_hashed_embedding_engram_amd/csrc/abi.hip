@@ -143,6 +143,10 @@ int32_t dispatch_project(const uint16_t *x, const uint16_t *w, uint16_t *y, int6
 {
     if (T == 0)
         return ENGRAM_OK;
+    if (T == 1 && K <= kGemvMaxK)
+        return launch_gemv(x, w, y, T, K, N, l);
+    if (gemm_small_fits(T, K, N))
+        return launch_gemm_small(x, w, y, T, K, N, l);
     if (T <= kGemvMaxT && K <= kGemvMaxK)
         return launch_gemv(x, w, y, T, K, N, l);
     return launch_gemm(x, w, y, T, K, N, l);

@@ -1,0 +1,170 @@
+// Stage 3 for a few tokens (2..64): the wkv projection as a bf16 MFMA GEMM
+// with a short token dimension (atlascybernetics "spark_model/layers/
+// engram_v41.rs", module doc stage 3; metrale "deepseek_v41_ref/engram.rs",
+// linear_bf16) -- several sequences' decode tokens, short prompts.
+//
+// C[M][N] = A[M][K] * B[N][K]^T with A = the tokens (M <= 64), B = wkv.  At
+// this M the GEMM is a single pass over wkv (252 MB at the decode shape), so
+// the kernel is laid out like a weight stream: one 256-thread workgroup per
+// CU owns 16*RT consecutive output rows (RT <= 6) for all tokens, its four
+// wavefronts split K in four, and every lane streams its rows' weights
+// straight from HBM into v_mfma_f32_16x16x32_bf16 operands, two batches of
+// four K steps in flight.  The matrix-core "A" operand is wkv (16 rows), "B" the tokens (16
+// per tile, MT tiles), so each lane's accumulator holds 4 consecutive outputs
+// of one token (8-byte stores).
+//
+// K order: wavefront w takes K values [w*K/4, (w+1)*K/4) in steps of 32, and
+// a step hands lane group q (lanes 16q..16q+15) values 8q..8q+7 of it, so
+// one load instruction reads 64 contiguous bytes of each of 16 rows.  The
+// four wavefronts' partial sums meet in LDS and are added in wavefront order.
+#include "common.h"
+
+namespace engram {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSteps = 4;         // K steps (32 values) per batch of loads
+constexpr int kMaxRowTiles = 6;   // 16-row tiles per workgroup
+
+template <int RT, int MT>
+__global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restrict__ A,
+                                                         const uint16_t *__restrict__ B,
+                                                         uint16_t *__restrict__ C, int M, int N,
+                                                         int K)
+{
+    __shared__ f32x4 red[4][RT][MT][64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int n0 = blockIdx.x * 16 * RT;
+    const int nsteps = K >> 7;                 // 32-value steps of this wavefront
+    const int k0 = w * (K >> 2) + 8 * q;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // this lane's rows of wkv (clamped: tile rows past N read row N-1 and are
+    // never stored) and of the tokens (past M: zeros, no load)
+    const u32x4 *brow[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+        brow[rt] = (const u32x4 *)(B + (int64_t)min(n0 + 16 * rt + r16, N - 1) * K + k0);
+    const u32x4 *arow[MT];
+    bool avalid[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+        const int m = 16 * mt + r16;
+        avalid[mt] = m < M;
+        arow[mt] = (const u32x4 *)(A + (int64_t)(m < M ? m : 0) * K + k0);
+    }
+
+    f32x4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+            acc[rt][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    u32x4 wb[2][kSteps][RT], xb[2][kSteps][MT];
+    // a row's consecutive steps back to back: the second half of each cache
+    // line is read right after the first
+    auto load = [&](int set, int s0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+            for (int s = 0; s < kSteps; s++)
+                wb[set][s][rt] = brow[rt][4 * (s0 + s)];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int s = 0; s < kSteps; s++)
+                xb[set][s][mt] = avalid[mt] ? arow[mt][4 * (s0 + s)] : zero;
+    };
+    auto compute = [&](int set) {
+#pragma unroll
+        for (int s = 0; s < kSteps; s++)
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+                    acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wb[set][s][rt]),
+                        __builtin_bit_cast(bf16x8, xb[set][s][mt]), acc[rt][mt], 0, 0, 0);
+    };
+
+    // batches of kSteps steps, two in flight (nsteps is a multiple of 2*kSteps)
+    load(0, 0);
+    for (int s0 = 0; s0 < nsteps; s0 += 2 * kSteps) {
+        load(1, s0 + kSteps);
+        compute(0);
+        if (s0 + 2 * kSteps < nsteps)
+            load(0, s0 + 2 * kSteps);
+        compute(1);
+    }
+
+    // ---- the four K quarters meet in LDS, added in wavefront order
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+            red[w][rt][mt][lane] = acc[rt][mt];
+    __syncthreads();
+    // accumulator e of lane l: output n = 16*rt + 4*(l/16) + e, token 16*mt + l%16
+    for (int t = w; t < RT * MT; t += 4) {
+        const int rt = t / MT, mt = t - rt * MT;
+        const f32x4 v = ((red[0][rt][mt][lane] + red[1][rt][mt][lane]) + red[2][rt][mt][lane]) +
+                        red[3][rt][mt][lane];
+        const int m = 16 * mt + r16;
+        const int n = n0 + 16 * rt + 4 * q;
+        if (m < M && n < N) {
+            u32x2 o;
+            o.x = pack_bf16x2(v.x, v.y);
+            o.y = pack_bf16x2(v.z, v.w);
+            *(u32x2 *)(C + (int64_t)m * N + n) = o;
+        }
+    }
+}
+
+}  // namespace
+
+bool gemm_small_fits(int64_t M, int64_t K, int64_t N)
+{
+    return M >= 1 && M <= kGemmSmallMaxM && K % (128 * 2 * kSteps) == 0 && N % 16 == 0;
+}
+
+int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
+                          int64_t K, int64_t N, const Launch &l)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    // row tiles of 16 per workgroup: about one workgroup per CU (at most 6
+    // tiles: beyond that the operand registers spill at four token tiles)
+    const int64_t tiles = N / 16;
+    int rt = (int)((tiles + cus - 1) / cus);
+    if (rt > kMaxRowTiles)
+        rt = kMaxRowTiles;
+    const int mt = (int)((M + 15) / 16);
+    const dim3 grid((unsigned)((tiles + rt - 1) / rt)), block(256);
+#define ENGRAM_SMALL_CASE(R_, T_)                                                                \
+    if (rt == R_ && mt == T_) {                                                                  \
+        dispatch(gemm_small_kernel<R_, T_>, grid, block, l, true, true, x, w, y, (int)M, (int)N, \
+                 (int)K);                                                                        \
+        return launch_status("engram small gemm kernel");                                       \
+    }
+#define ENGRAM_SMALL_ROW(R_)                                                                     \
+    ENGRAM_SMALL_CASE(R_, 1) ENGRAM_SMALL_CASE(R_, 2) ENGRAM_SMALL_CASE(R_, 3)                   \
+    ENGRAM_SMALL_CASE(R_, 4)
+    ENGRAM_SMALL_ROW(1) ENGRAM_SMALL_ROW(2) ENGRAM_SMALL_ROW(3) ENGRAM_SMALL_ROW(4)
+    ENGRAM_SMALL_ROW(5) ENGRAM_SMALL_ROW(6)
+#undef ENGRAM_SMALL_ROW
+#undef ENGRAM_SMALL_CASE
+    return fail(ENGRAM_E_UNSUPPORTED, "engram small gemm: %lld tokens", (long long)M);
+}
+
+}  // namespace engram

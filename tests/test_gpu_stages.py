@@ -253,7 +253,19 @@ def test_project_gemv_decode_shape(E, decode, T):
     check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
 
 
-@pytest.mark.parametrize("M", [5, 64, 255, 257, 300, 513])
+@pytest.mark.parametrize("M", [2, 5, 16, 17, 33, 64])
+def test_project_small_decode_shape(E, decode, M):
+    """A few tokens (several sequences' decode tokens, short prompts) through
+    the decode-shape wkv: the MFMA GEMM laid out as a weight stream, every
+    output checked (partial token tiles at M = 5, 17, 33)."""
+    rng = np.random.default_rng(100 + M)
+    ids = rng.integers(0, decode.layers[0]["rows"], size=(M, 24))
+    x = decode.oracle_rows(0, ids).reshape(M, -1)
+    log(f"project small: M={M} K=6144 N=20480")
+    check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
+
+
+@pytest.mark.parametrize("M", [2, 5, 64, 255, 257, 300, 513])
 def test_project_gemm_tiny_shape(E, tiny, M):
     rng = np.random.default_rng(M)
     x = bf16_rand(rng, (M, tiny.w.K), 0.5)
