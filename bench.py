@@ -50,15 +50,26 @@ def log(*a):
 
 def source_digest(name):
     """First 16 hex digits of the SHA-256 of a kernel source followed by the
-    shared header it includes, with // comments and blank lines removed (a
-    comment edit does not change the kernel)."""
+    library headers it includes (recursively, each once, in include order),
+    with // comments and blank lines removed (a comment edit does not change
+    the kernel)."""
     h = hashlib.sha256()
-    for f in (name, "common.h"):
+    seen = []
+
+    def add(f):
+        if f in seen:
+            return
+        seen.append(f)
         with open(os.path.join(CSRC, f)) as fh:
             for line in fh:
+                m = re.match(r'\s*#include "([^"]+)"', line)
+                if m and os.path.exists(os.path.join(CSRC, m.group(1))):
+                    add(m.group(1))
                 code = re.sub(r"//.*", "", line).rstrip()
                 if code:
                     h.update(code.encode() + b"\n")
+
+    add(name)
     return h.hexdigest()[:16]
 
 
@@ -448,6 +459,7 @@ def main():
             "kernel": "decode_q2kw_kernel<Q2K,6> (hash + gather/dequant + projection off the "
                       "Q2_K wkv blocks; vector-ALU bound)",
             "bytes_per_launch": decq["proj_bytes"], "avg_launch_ms": decq["proj_avg_ms"],
+            "traffic": counter_traffic("decode_q2kw_counters.md", "decode.hip"),
             "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
             "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
             "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
