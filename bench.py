@@ -10,9 +10,14 @@ engram tokens/s per layer = steps * layers / seconds, inputs resident in HBM.
 The same steps through the staged kernels (hash, gather, GEMV, gate) are
 reported under "decode_staged".
 
-Also measured in the same run: the prefill workload (T = 4096 Zipf tokens,
-both layers, one hash pass; projection on the MFMA GEMM), reported under
-"prefill" with its own roofline.
+Also measured in the same run: the decode workload with wkv as Q2_K blocks
+("decode_wkv_q2k"), several sequences decoded together ("decode_batched"),
+the prefill workload (T = 4096 Zipf tokens, both layers, one hash pass;
+projection on the MFMA GEMM) under "prefill" with its own roofline, the
+large-table gather workload (6.3 GB Q2_K table, T = 16384 uniform tokens;
+gather + dequant GB/s apart from the GEMM) under "gather_stress", and the
+e4m3 prefill/decode split (four 2048-token calls, then 128 single-token
+steps) under "split_e4m3".
 
 Per-kernel durations come from HIP events the runtime records with each
 kernel dispatch (engram_ctx_set_timing) during a second pass over the same
@@ -316,6 +321,110 @@ def bench_prefill(args, torch, E, G, synth):
     )
 
 
+def bench_gather_stress(args, torch, E, G, synth):
+    """The large-table workload (one Q2_K layer of ~75 M rows, 6.3 GB; T
+    16384 uniform tokens, so every row read is a random 84-byte block):
+    whole forwards, with the gather + dequant rate reported apart from the
+    projection GEMM."""
+    w = synth.GATHER_Q2K
+    log(f"gather stress: generating {w.name}")
+    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    del host
+    T = w.prompt
+    reps, warm = args.stress_steps, 1
+    ids = G.token_ids(w)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    h = torch.from_numpy(G.highway(w, T)).cuda()
+    ctx = make_ctx(E, w, tables, layers, T, T * (warm + 2 * reps))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(w.n_layers):
+            ctx.forward(l, d_ids, T, h)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ctx.set_timing(True)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    stages = ctx.timing()
+    ctx.check()
+    avg = {k: v[0] / max(1, v[1]) for k, v in stages.items()}
+    gather_bytes = T * w.cols * (8 + 84 + w.head_dim * 2)
+    gbps = gather_bytes / (avg["gather"] / 1e3) / 1e9
+    tflops = 2.0 * T * w.K * w.N / (avg["project"] / 1e3) / 1e12
+    rows = int(ht["offsets"][0][-1] + ht["primes"][0][-1])
+    del ctx
+    return dict(
+        workload=w.name, T=T, layers=w.n_layers, table_rows=rows, table_bytes=rows * 84,
+        ms_per_step=ms / reps, value=reps * T * w.n_layers / (ms / 1e3),
+        unit="engram tokens/s per layer", stages_ms=avg,
+        gather=dict(bound="hbm", kernel="gather_q2k_kernel (random 84-byte rows -> bf16)",
+                    bytes_per_launch=gather_bytes, avg_launch_ms=avg["gather"],
+                    achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s", frac=gbps / HBM_PEAK_GBPS,
+                    traffic=counter_traffic("gather_stress_counters.md", "gather.hip")),
+        project=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                     frac=tflops / BF16_PEAK_TFLOPS))
+
+
+def bench_split(args, torch, E, G, synth):
+    """The e4m3 prefill/decode split: 8192 Zipf tokens as four 2048-token
+    calls, then 128 single-token steps, both layers, the look-back carried
+    across every call.  A pass starts from a reset history; tokens/s per
+    layer reported for each phase."""
+    w = synth.SPLIT_E4M3
+    log(f"split: generating {w.name}")
+    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    del host
+    ids = G.token_ids(w)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    chunks = [d_ids[c:c + w.chunk] for c in range(0, w.prompt, w.chunk)]
+    steps = [d_ids[w.prompt + i:w.prompt + i + 1] for i in range(w.decode_steps)]
+    hp = torch.from_numpy(G.highway(w, w.chunk)).cuda()
+    hd = torch.from_numpy(G.highway(w, w.decode_steps, decode=True)).cuda()
+    ctx = make_ctx(E, w, tables, layers, w.chunk, w.prompt + w.decode_steps)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    pre_ms = dec_ms = 0.0
+    for p in range(1 + args.split_passes):
+        ctx.reset()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for c in chunks:
+            for l in range(w.n_layers):
+                ctx.forward(l, c, w.chunk, hp)
+        ev[1].record(stream)
+        for i, t in enumerate(steps):
+            for l in range(w.n_layers):
+                ctx.forward(l, t, 1, hd[i:i + 1])
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if p:
+            pre_ms += ev[0].elapsed_time(ev[1])
+            dec_ms += ev[1].elapsed_time(ev[2])
+    ctx.check()
+    del ctx
+    n = args.split_passes
+    return dict(
+        workload=w.name, layers=w.n_layers, prompt=w.prompt, chunk=w.chunk,
+        decode_steps=w.decode_steps, passes=n,
+        prefill=dict(ms_per_chunk=pre_ms / (n * len(chunks)),
+                     value=n * w.prompt * w.n_layers / (pre_ms / 1e3),
+                     unit="engram tokens/s per layer"),
+        decode=dict(ms_per_step=dec_ms / (n * w.decode_steps),
+                    value=n * w.decode_steps * w.n_layers / (dec_ms / 1e3),
+                    unit="engram tokens/s per layer"))
+
+
 def cpu_baseline(res, synth, budget_s):
     """The oracle on the host cores over the first decode steps (both
     layers), until budget_s seconds of work have run."""
@@ -353,13 +462,18 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the many-token legs (prefill, gather stress, e4m3 split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--batch-sequences", type=int, nargs="*", default=[4],
                     help="also decode this many sequences together (one weight pass per step)")
     ap.add_argument("--no-decode", action="store_true",
                     help="run only the prefill measurement (for counter passes)")
+    ap.add_argument("--stress-steps", type=int, default=3)
+    ap.add_argument("--split-passes", type=int, default=2)
+    ap.add_argument("--only-stress", action="store_true",
+                    help="run only the gather-stress measurement (for counter passes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy of BYTES bytes (read BYTES, write "
                          "BYTES) three times: the calibration kernel for the HBM counters")
@@ -392,6 +506,10 @@ def main():
     if args.no_decode:
         print(json.dumps({"prefill": bench_prefill(args, torch, E, G, synth)}), flush=True)
         return
+    if args.only_stress:
+        print(json.dumps({"gather_stress": bench_gather_stress(args, torch, E, G, synth)}),
+              flush=True)
+        return
     inputs = device_inputs(synth.DECODE_Q2K, torch, E, G)
     dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=inputs)
     log(f"decode (fused): {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
@@ -417,6 +535,14 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
     if pre:
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
+    stress = split = None
+    if not args.no_prefill:
+        stress = bench_gather_stress(args, torch, E, G, synth)
+        log(f"gather stress: {stress['ms_per_step']:.3f} ms/step, gather "
+            f"{stress['gather']['achieved']:.0f} GB/s, stages(ms) {stress['stages_ms']}")
+        split = bench_split(args, torch, E, G, synth)
+        log(f"split: prefill {split['prefill']['ms_per_chunk']:.3f} ms/chunk, decode "
+            f"{split['decode']['ms_per_step'] * 1e3:.1f} us/step")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
@@ -466,6 +592,8 @@ def main():
                        "stages_ms_per_layer_step": decq_staged["stages"]}},
         "decode_batched": batched,
         "prefill": pre,
+        "gather_stress": stress,
+        "split_e4m3": split,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

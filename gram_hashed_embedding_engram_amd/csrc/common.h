@@ -105,18 +105,58 @@ __device__ __forceinline__ u32x4 e4m3_dequant8(uint32_t w0, uint32_t w1, float s
     return o;
 }
 
-// acc + sum of the 8 products of two rows of 8 bf16 values (f32 fma chain).
-__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
+// ---- the summation order of every one-token projection
+//
+// Lane l of the wavefront that owns an output row takes the row's 16-value
+// sub-blocks g = l, l+64, l+128, ... (8-value chunks 2g and 2g+1).  In a
+// sub-block the bf16 pairs 0, 2, 4, 6 go into one f32 partial sum and the
+// pairs 1, 3, 5, 7 into another, one v_dot2_f32_bf16 per pair, in that
+// order; the lane's two sums are added, then the 64 lane sums by wave_sum.
+// The bf16 GEMV, the one-launch decode kernel and the kernels over Q2_K wkv
+// blocks all follow it, so a row gives the same bits whether its weights
+// arrive as bf16 or as the Q2_K blocks they expand to.
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + w.lo*x.lo + w.hi*x.hi for two packed bf16 pairs.
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc)
 {
-    acc = fmaf(bf16_lo(w.x), bf16_lo(x.x), acc);
-    acc = fmaf(bf16_hi(w.x), bf16_hi(x.x), acc);
-    acc = fmaf(bf16_lo(w.y), bf16_lo(x.y), acc);
-    acc = fmaf(bf16_hi(w.y), bf16_hi(x.y), acc);
-    acc = fmaf(bf16_lo(w.z), bf16_lo(x.z), acc);
-    acc = fmaf(bf16_hi(w.z), bf16_hi(x.z), acc);
-    acc = fmaf(bf16_lo(w.w), bf16_lo(x.w), acc);
-    acc = fmaf(bf16_hi(w.w), bf16_hi(x.w), acc);
-    return acc;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+
+// One sub-block: weights wa, wb (chunks 2g, 2g+1) against activations xa, xb.
+__device__ __forceinline__ void subblock_dot(const u32x4 &wa, const u32x4 &wb, const u32x4 &xa,
+                                             const u32x4 &xb, float &acc, float &acc2)
+{
+    acc = dot2(wa.x, xa.x, acc);
+    acc2 = dot2(wa.y, xa.y, acc2);
+    acc = dot2(wa.z, xa.z, acc);
+    acc2 = dot2(wa.w, xa.w, acc2);
+    acc = dot2(wb.x, xb.x, acc);
+    acc2 = dot2(wb.y, xb.y, acc2);
+    acc = dot2(wb.z, xb.z, acc);
+    acc2 = dot2(wb.w, xb.w, acc2);
+}
+
+// A bf16 row read as NI coalesced 1 KiB loads (lane l holds chunk 64m + l of
+// load m) is brought into sub-block order through the wavefront's own 2 KiB
+// LDS buffer `stage`, one 128-chunk segment (loads 2s, 2s+1) at a time:
+// f(s, a, b) then gets chunks 2g, 2g+1 of sub-block g = 64s + lane, for the
+// lanes with g < n_sb.  Only this wavefront touches `stage`, and a
+// wavefront's LDS accesses execute in program order, so no barrier is needed.
+template <int NI, class F>
+__device__ __forceinline__ void for_each_subblock(const u32x4 (&wv)[NI], u32x4 *stage, int lane,
+                                                  int n_sb, F f)
+{
+#pragma unroll
+    for (int s = 0; s < (NI + 1) / 2; s++) {
+        stage[lane] = wv[2 * s];
+        if (2 * s + 1 < NI)
+            stage[64 + lane] = wv[2 * s + 1];
+        if (64 * s + lane < n_sb)
+            f(s, stage[2 * lane], stage[2 * lane + 1]);
+    }
 }
 
 // v + (v of the lane that DPP control CTRL selects; 0 in rows outside ROWS).

@@ -7,16 +7,19 @@
 //
 // At one token the layer is one pass over wkv (252 MB at the decode shape);
 // hashing 24 ids and dequantising 24 rows is a few microseconds of latency.
-// Fused, that latency hides under the weight stream: every wavefront first
-// puts its first wkv row in flight, then its workgroup hashes the token (one
-// thread per (layer, column)), stages the needed 84-byte Q2_K blocks in LDS
-// with coalesced dword loads, expands them once per workgroup into the
-// token's bf16 activations (12 KiB of LDS), which the wavefronts read back
+// Fused, that latency hides under the weight stream: every thread first reads
+// its hash constants, every wavefront then puts its first wkv row in flight,
+// and its workgroup hashes the token (one thread per (layer, column)),
+// stages the needed 84-byte Q2_K blocks in LDS through the scalar cache (the
+// token, its look-back and the blocks are scalar loads, which do not wait
+// behind the weight loads in flight), expands them once per workgroup into
+// the token's bf16 activations (12 KiB of LDS), which the wavefronts read back
 // per row (registers hold only the weight row in flight, so four workgroups
 // stay resident per CU).  The projection loop is the GEMV's: one wavefront
-// per output row at a time, K/512 non-temporal 1 KiB loads in flight, one
-// f32 wave sum, one bf16 rounding, the store issued after the next row's
-// loads.  Workgroup 0 also writes the step's row ids, the dequantised rows
+// per output row at a time, K/512 non-temporal 1 KiB loads in flight, the
+// row brought into the one-token sub-block order of common.h through the
+// wavefront's 2 KiB LDS buffer, one f32 wave sum, one bf16 rounding, the
+// store issued after the next row's loads.  Workgroup 0 also writes the step's row ids, the dequantised rows
 // and the history entry, so the workspace holds what the separate stages
 // would have left there.
 //
@@ -55,53 +58,107 @@ struct DecodeArgs {
     int32_t *err;
 };
 
+// A load of a value that no thread writes during the launch, through the
+// scalar cache (constant address space; the address must be the same in every
+// lane).  Vector loads complete in issue order, so a vector load issued after
+// the weight row's loads cannot be waited for without waiting for the row;
+// scalar loads have their own counter and do not queue behind it.
+template <class T>
+__device__ __forceinline__ T cload(const T *p)
+{
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The hash constants of the slot thread tid computes (layer tid / cols,
+// column tid % cols).  Indexed per thread, they arrive by vector loads, so a
+// decode kernel reads them first, before its first weight row: the wait for
+// them then leaves the row's loads in flight.
+struct SlotConsts {
+    int64_t m[ENGRAM_MAX_NGRAM];
+    int64_t prime, offset;
+};
+
+__device__ __forceinline__ SlotConsts slot_consts(const HashConsts &c)
+{
+    SlotConsts sc;
+    const int slot = min((int)threadIdx.x, c.nl * c.cols - 1);
+    const int l = slot / c.cols;
+#pragma unroll
+    for (int k = 0; k < ENGRAM_MAX_NGRAM; k++)      // in bounds: l*ng + k < MAX_LAYERS*MAX_NGRAM
+        sc.m[k] = c.mult[l * c.ng + k];
+    sc.prime = c.prime[slot];
+    sc.offset = c.offset[slot];
+    return sc;
+}
+
 // Hash of the token and gather + dequant of this layer's cols rows into the
 // activations s_x by the NT threads of a workgroup (every workgroup;
 // workgroup 0 also writes the row ids, the history entry and the dequantised
-// rows).  Ends with s_x complete.
+// rows).  Ends with s_x complete.  The token, its look-back and (Q2_K) the
+// table blocks come through the scalar cache, so nothing here waits for the
+// weight loads the kernel has in flight.
 template <int FMT, int NT>
 __device__ __forceinline__ void decode_prologue(const HashConsts &c, const DecodeArgs &a,
-                                                int64_t *s_id, uint32_t *s_blk, u32x4 *s_x)
+                                                const SlotConsts &sc, int64_t *s_id,
+                                                uint32_t *s_blk, u32x4 *s_x)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, and known so
     const int cols = c.cols;
     const int64_t kc = (int64_t)cols * 32;
     const int64_t pos = a.pos;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // ---- the token's compressed id and its look-back (win[k]: k positions
+    // back; -1 = unmapped or before the sequence start), the same in every thread
+    int64_t win[ENGRAM_MAX_NGRAM];
+    bool bad = false;
+    if (a.first_layer) {
+        const int32_t t = cload(a.ids);
+        bad = t < 0 || (int64_t)t >= c.vocab;
+        const int64_t mapped = cload(a.token_map + (bad ? 0 : t));
+        win[0] = bad ? -1 : mapped;          // reported, then hashed as unmapped
+    } else {
+        win[0] = cload(a.history + pos);
+    }
+#pragma unroll
+    for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
+        win[k] = -1;
+        if (k < c.ng) {
+            const int64_t q = pos - k;
+            const int64_t v = cload(a.history + (q >= 0 ? q : 0));
+            win[k] = q >= 0 ? v : -1;
+        }
+    }
 
     // ---- hash: thread (l, col) computes layer l's id of column col; every
     // workgroup needs its own layer's, workgroup 0 of the first layer writes all
     if (tid < c.nl * cols) {
         const int l = tid / cols, col = tid - l * cols;
         if (l == a.layer || (blockIdx.x == 0 && a.first_layer)) {
-            int64_t own;
-            bool bad = false;
-            if (a.first_layer) {
-                const int32_t t = a.ids[0];
-                bad = t < 0 || (int64_t)t >= c.vocab;
-                own = bad ? -1 : a.token_map[t];     // reported, then hashed as unmapped
-            } else {
-                own = a.history[pos];
-            }
             const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
-            bool blocked = own == -1;
-            const int64_t *m = c.mult + l * c.ng;
-            uint64_t r = (uint64_t)(blocked ? c.pad_id : own) * (uint64_t)m[0];
+            bool blocked = win[0] == -1;
+            uint64_t r = (uint64_t)(blocked ? c.pad_id : win[0]) * (uint64_t)sc.m[0];
 #pragma unroll
             for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
                 if (k < ngram) {
-                    const int64_t q = pos - k;
-                    const int64_t src = q >= 0 ? a.history[q] : 0;
-                    blocked = blocked || q < 0 || src == -1;
-                    r ^= (uint64_t)(blocked ? c.pad_id : src) * (uint64_t)m[k];
+                    blocked = blocked || win[k] == -1;
+                    r ^= (uint64_t)(blocked ? c.pad_id : win[k]) * (uint64_t)sc.m[k];
                 }
             }
             const int slot = l * cols + col;
-            const int64_t id = rem_euclid((int64_t)r, c.prime[slot]) + c.offset[slot];
+            const int64_t id = rem_euclid((int64_t)r, sc.prime) + sc.offset;
             if (blockIdx.x == 0) {
                 a.row_ids[slot] = id;
                 if (tid == 0 && a.first_layer) {
-                    a.history[pos] = own;
+                    a.history[pos] = win[0];
                     if (bad && a.err)
                         atomicOr(a.err, ENGRAM_DEVERR_TOKEN);
                 }
@@ -118,11 +175,39 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
 
     // ---- gather + dequant of the cols rows into the activations in LDS
     if (FMT == ENGRAM_FMT_Q2K) {
-        for (int i = tid; i < cols * 21; i += NT) {
-            const int r = i / 21, d = i - r * 21;
-            const int64_t id = s_id[r];
-            s_blk[i] = id >= 0 ? *(const uint32_t *)(a.table + id * ENGRAM_Q2K_ROW_BYTES + 4 * d)
-                               : 0u;
+        // wavefront w stages blocks w, w + NW, ...: a batch of kBatch blocks'
+        // 21 dwords at a time by scalar loads (all issued before the first is
+        // used: one memory round trip a batch), into lanes 0..20, then LDS.
+        // A missing block (id -1) reads block 0 and stores zeros.  Three
+        // blocks take 63 SGPRs: the 1024-thread kernel (at most two blocks a
+        // wavefront, fewer SGPRs at its occupancy) batches two.
+        constexpr int NW = NT / 64, kBatch = NW >= 16 ? 2 : 3;
+        for (int r0 = wid; r0 < cols; r0 += kBatch * NW) {
+            int64_t id[kBatch];
+            const uint32_t *blk[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                const int r = r0 + b * NW;
+                id[b] = r < cols ? uniform64(s_id[r]) : -1;
+                blk[b] = (const uint32_t *)(a.table + (id[b] >= 0 ? id[b] : 0) *
+                                                          ENGRAM_Q2K_ROW_BYTES);
+            }
+            uint32_t d[kBatch][21];
+#pragma unroll
+            for (int b = 0; b < kBatch; b++)
+#pragma unroll
+                for (int j = 0; j < 21; j++)
+                    d[b][j] = cload(blk[b] + j);
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                uint32_t v = 0u;
+#pragma unroll
+                for (int j = 0; j < 21; j++)      // dword j into lane j (v_writelane)
+                    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(d[b][j]), "i"(j));
+                const int r = r0 + b * NW;
+                if (r < cols && lane < 21)
+                    s_blk[r * 21 + lane] = id[b] >= 0 ? v : 0u;
+            }
         }
         __syncthreads();
         for (int ch = tid; ch < kc; ch += NT) {
@@ -155,25 +240,27 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
     __shared__ int64_t s_id[kDecodeMaxCols];
     __shared__ uint32_t s_blk[kDecodeMaxCols * 21];
     __shared__ u32x4 s_x[kMaxChunks];
+    __shared__ u32x4 s_stage[4][128];
     const int tid = threadIdx.x, lane = tid & 63;
     const int64_t K = (int64_t)c.cols * 256, kc = K >> 3, N = a.N;
+    const int n_sb = c.cols * 16;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + tid) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     uint16_t *__restrict__ y = a.y;
 
-    // ---- the first wkv row of this wavefront goes out before anything else
+    // ---- this thread's hash constants, then the first wkv row of this
+    // wavefront (past the row's end, lanes load its last chunk again: loads
+    // are unconditional, and the staged order never reads those chunks)
+    const SlotConsts sc = slot_consts(c);
     u32x4 wv[NI];
     {
         const u32x4 *wr = (const u32x4 *)(w + min(wave, N - 1) * K);
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
-            const int64_t idx = (int64_t)i * 64 + lane;
-            wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
-        }
+        for (int i = 0; i < NI; i++)
+            wv[i] = __builtin_nontemporal_load(wr + min((int64_t)i * 64 + lane, kc - 1));
     }
 
-    decode_prologue<FMT, 256>(c, a, s_id, s_blk, s_x);
+    decode_prologue<FMT, 256>(c, a, sc, s_id, s_blk, s_x);
 
     // ---- projection: rows wave, wave + n_waves, ...  A row's result is
     // stored after the next row's loads are issued, so the loop's wait for
@@ -184,22 +271,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
         if (n != wave) {
             const u32x4 *wr = (const u32x4 *)(w + n * K);
 #pragma unroll
-            for (int i = 0; i < NI; i++) {
-                const int64_t idx = (int64_t)i * 64 + lane;
-                wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
-            }
+            for (int i = 0; i < NI; i++)
+                wv[i] = __builtin_nontemporal_load(wr + min((int64_t)i * 64 + lane, kc - 1));
         }
         if (lane == 0 && prev_n >= 0)
             y[prev_n] = prev_v;
-        // the activations stay in LDS (16-byte reads, consecutive lanes):
-        // registers hold only the weight row in flight
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NI; i++) {
-            const int64_t idx = (int64_t)i * 64 + lane;
-            acc = dot8(wv[i], idx < kc ? s_x[idx] : zero, acc);
-        }
-        prev_v = f32_to_bf16(wave_sum(acc));
+        // the activations stay in LDS: registers hold only the weight row in
+        // flight
+        float acc = 0.0f, acc2 = 0.0f;
+        for_each_subblock<NI>(wv, s_stage[tid >> 6], lane, n_sb,
+                              [&](int s, const u32x4 &wa, const u32x4 &wb) {
+                                  const int g = 64 * s + lane;
+                                  subblock_dot(wa, wb, s_x[2 * g], s_x[2 * g + 1], acc, acc2);
+                              });
+        prev_v = f32_to_bf16(wave_sum(acc + acc2));
         prev_n = n;
     }
     if (lane == 0 && prev_n >= 0)
@@ -230,11 +315,12 @@ __global__ __launch_bounds__(kQ2kwThreads, 8) void decode_q2kw_kernel(const Hash
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const uint32_t *wd = (const uint32_t *)wq;
 
-    // ---- the first row's blocks go out before anything else
+    // ---- this thread's hash constants, then the first row's blocks
+    const SlotConsts sc = slot_consts(c);
     uint32_t r[NLD];
     q2k_row_load<NLD>(wd + min(wave, N - 1) * row_dwords, row_dwords, lane, r);
 
-    decode_prologue<FMT, kQ2kwThreads>(c, a, s_id, s_blk, s_x);
+    decode_prologue<FMT, kQ2kwThreads>(c, a, sc, s_id, s_blk, s_x);
 
     // ---- projection, one row per wavefront at a time
     for (int64_t n = wave; n < N; n += n_waves) {

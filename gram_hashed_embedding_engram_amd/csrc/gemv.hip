@@ -7,9 +7,12 @@
 //
 // Layout: w [N][K] bf16, K contiguous.  One wavefront owns one output row at
 // a time and reads it as K/512 coalesced 1 KiB loads (16 bytes a lane, all
-// issued before the first is consumed, to keep many bytes in flight).  The
-// activations x [T][K] are loaded once per wave into registers, lane l
-// holding elements 8*(64*i + l) .. +7 of step i.  Waves are persistent and
+// issued before the first is consumed, to keep many bytes in flight); the
+// row then passes through the wavefront's 2 KiB LDS buffer into the
+// sub-block order common.h fixes for one-token projections, so results equal
+// those of the projection over Q2_K wkv blocks bit for bit.  The activations
+// x [T][K] are loaded once per wave into registers in that order (lane l:
+// chunks 2g, 2g+1 of sub-blocks g = l, l+64, ...).  Waves are persistent and
 // take rows wave_id, wave_id + n_waves, ...  The per-lane f32 partial sums
 // are reduced across the wave; the sum is rounded once to bf16.
 #include "common.h"
@@ -19,29 +22,33 @@ namespace {
 
 constexpr int kGemvBlocksPerCu = 4;
 
-
 template <int NT, int NI>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ w,
                                                    uint16_t *__restrict__ y, int64_t K, int64_t N)
 {
-    const int lane = threadIdx.x & 63;
+    constexpr int NS = (NI + 1) / 2;                 // 128-chunk segments of a row
+    __shared__ u32x4 s_stage[4][128];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t kc = K >> 3;                       // 16-byte chunks per row
+    const int n_sb = (int)(K >> 4);                  // 16-value sub-blocks per row
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
 
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 xr[NT][NI];
+    u32x4 xr[NT][2 * NS];
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         const u32x4 *xt = (const u32x4 *)(x + t * K);
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
-            const int64_t idx = (int64_t)i * 64 + lane;
-            xr[t][i] = idx < kc ? xt[idx] : zero;
+        for (int s = 0; s < NS; s++) {
+            const int g = 64 * s + lane;
+            xr[t][2 * s] = g < n_sb ? xt[2 * g] : zero;
+            xr[t][2 * s + 1] = g < n_sb ? xt[2 * g + 1] : zero;
         }
     }
 
+    u32x4 *stage = s_stage[wid];
     for (int64_t n = wave; n < N; n += n_waves) {
         const u32x4 *wr = (const u32x4 *)(w + n * K);
         u32x4 wv[NI];
@@ -50,18 +57,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ 
             const int64_t idx = (int64_t)i * 64 + lane;
             wv[i] = idx < kc ? __builtin_nontemporal_load(wr + idx) : zero;
         }
-        float acc[NT];
+        float acc[NT], acc2[NT];
 #pragma unroll
         for (int t = 0; t < NT; t++)
-            acc[t] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NI; i++)
+            acc[t] = acc2[t] = 0.0f;
+        for_each_subblock<NI>(wv, stage, lane, n_sb, [&](int s, const u32x4 &a, const u32x4 &b) {
 #pragma unroll
             for (int t = 0; t < NT; t++)
-                acc[t] = dot8(wv[i], xr[t][i], acc[t]);
+                subblock_dot(a, b, xr[t][2 * s], xr[t][2 * s + 1], acc[t], acc2[t]);
+        });
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            const float s = wave_sum(acc[t]);
+            const float s = wave_sum(acc[t] + acc2[t]);
             if (lane == t)
                 y[t * N + n] = f32_to_bf16(s);
         }

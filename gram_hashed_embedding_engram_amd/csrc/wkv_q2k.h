@@ -29,8 +29,6 @@
 
 namespace engram {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 constexpr int kQ2kMaxSubBlocks = 8;                       // sub-blocks per lane: K <= 8192
 constexpr int kQ2kWkvMaxRowDwords = 21 * (8192 / 256);    // 672
 
@@ -43,10 +41,8 @@ __device__ __forceinline__ void q2k_row_load(const uint32_t *__restrict__ row, i
                                              int lane, uint32_t (&r)[NLD])
 {
 #pragma unroll
-    for (int j = 0; j < NLD; j++) {
-        const int idx = j * 64 + lane;
-        r[j] = idx < row_dwords ? __builtin_nontemporal_load(row + idx) : 0u;
-    }
+    for (int j = 0; j < NLD; j++)     // past the row's end: its last dword again (never staged)
+        r[j] = __builtin_nontemporal_load(row + min(j * 64 + lane, row_dwords - 1));
 }
 
 template <int NLD>
@@ -65,8 +61,9 @@ __device__ __forceinline__ void q2k_row_stage(uint32_t *lds, const uint32_t (&r)
 // g = lane + 64*i < n_sb (n_sb = K/16, so only the last round, i = NSB-1,
 // can leave lanes idle).  xs = the token's activations in LDS as 8-value
 // chunks (chunks 2g, 2g+1 belong to sub-block g); lds = the row's blocks, 21
-// dwords each.  Two partial sums (the first and second weight pair of every
-// four) shorten the dependency chain.
+// dwords each.  The order is the one-token projection order of common.h
+// (pairs 0, 2, 4, 6 of a sub-block into acc, 1, 3, 5, 7 into acc2), so the
+// result equals the bf16 GEMV's over the expanded weights bit for bit.
 template <int NSB>
 __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const u32x4 *xs, int n_sb,
                                              int lane)
@@ -106,12 +103,8 @@ __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const u32x4 *x
             const uint32_t hi = __builtin_amdgcn_perm(0u, pool_hi, u);   // high bytes
             const uint32_t wa = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // values 4j, 4j+1
             const uint32_t wb = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // values 4j+2, 4j+3
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wa),
-                                                  __builtin_bit_cast(bf16x2_t, x[2 * j]), acc,
-                                                  false);
-            acc2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wb),
-                                                   __builtin_bit_cast(bf16x2_t, x[2 * j + 1]),
-                                                   acc2, false);
+            acc = dot2(wa, x[2 * j], acc);
+            acc2 = dot2(wb, x[2 * j + 1], acc2);
         }
     }
     return acc + acc2;

@@ -180,9 +180,9 @@ int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, 
  * the raw blocks: 84 bytes per 256 weights instead of 512).  Weight k of
  * output row n is value k%256 of block k/256 of that row, decoded as a table
  * row is (bf16(d*scale*q - dmin*min)); the sum is f32, rounded once to bf16.
- * Results agree with engram_project over the bf16 expansion
- * (engram_dequant_q2k) to the rounding of the f32 sum, not bit for bit: the
- * two kernels add in different orders.
+ * Results equal engram_project's at one token over the bf16 expansion
+ * (engram_dequant_q2k) bit for bit: both add the products in the same order
+ * (the pages' byte-identical results).
  *   d_x [T][K] bf16 (16-byte aligned), d_wkv_q2k [N][K/256][84] (4-byte
  *   aligned), d_y [T][N] bf16; T in 0..1 (more tokens: ENGRAM_E_UNSUPPORTED,
  *   use engram_project); K a multiple of 256 up to 8192. */

@@ -334,6 +334,34 @@ def test_fused_decode_matches_staged(E, name):
     np.testing.assert_array_equal(calls[-1][0], want[-1:])
 
 
+def test_wkv_q2k_forward_matches_bf16_expansion(E):
+    """The decode workload with Q2_K wkv: every step through the kernels over
+    the blocks (one launch or staged) leaves exactly what the bf16 kernels
+    over the expanded wkv leave (row ids, rows, kv, highway) -- the pages'
+    byte-identical results."""
+    dev = Device(synth.DECODE_WKVQ2K.name)
+    w = dev.w
+    prompt, steps = 8, 24
+    log(f"Q2_K wkv vs bf16 expansion: {w.name}, prompt {prompt} + {steps} steps")
+    ids = G.token_ids(w, prompt + steps)
+    hp = G.highway(w, prompt)
+    hs = G.highway(w, steps, decode=True)
+    res = []
+    for blocks in (True, False):
+        for fused in (True, False):
+            ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps)
+            if not blocks:
+                for l in range(w.n_layers):
+                    ctx.set_wkv_q2k(l, None)
+            ctx.set_fused_decode(fused)
+            res.append(run_steps(dev, ctx, ids, steps, prompt, hp, hs))
+            ctx.check()
+    for r in res[1:]:
+        for i, (a, b) in enumerate(zip(res[0], r)):
+            for x, y, what in zip(a, b, ("row ids", "rows", "kv", "highway")):
+                np.testing.assert_array_equal(x, y, err_msg=f"call {i}: {what}")
+
+
 def test_fused_decode_bad_token(E):
     w = synth.TINY_E4M3
     dev = Device(w.name)

@@ -317,6 +317,10 @@ def test_dequant_q2k_exact(E):
 
 
 def check_project_q2k(E, x, blocks_host, blocks_dev=None, expanded=None, sample=None):
+    """The projection off the blocks against the oracle (over the oracle's
+    expansion) within the projection tolerance, and against the library's
+    bf16 GEMV over the library's expansion of the same blocks bit for bit (the
+    pages claim byte-identical results for the two)."""
     import oracle
     K = x.shape[1]
     N = blocks_host.shape[0]
@@ -325,6 +329,18 @@ def check_project_q2k(E, x, blocks_host, blocks_dev=None, expanded=None, sample=
     y = torch.empty(1, N, dtype=torch.int16, device="cuda")
     E.project_q2k(cuda(x), blocks_dev, y)
     got = to_np_u16(y)[0]
+    # engram_project takes N in multiples of 16: zero blocks pad the rows
+    n16 = -(-N // 16) * 16
+    padded = torch.zeros(n16, K // 256, 84, dtype=torch.uint8, device="cuda")
+    padded[:N] = blocks_dev.view(N, K // 256, 84)
+    bf = torch.empty(n16, K, dtype=torch.int16, device="cuda")
+    E.dequant_q2k(padded, bf)
+    y_bf = torch.empty(1, n16, dtype=torch.int16, device="cuda")
+    E.project(cuda(x), bf, y_bf)
+    np.testing.assert_array_equal(got, to_np_u16(y_bf)[0, :N],
+                                  err_msg="Q2_K-wkv projection differs from the bf16 GEMV")
+    del padded
+    del bf
     rows = np.arange(N) if sample is None else sample
     w = oracle.expand_q2k_matrix(blocks_host[rows]) if expanded is None else expanded[rows]
     want = oracle.linear_bf16(x, w)[0]
