@@ -14,7 +14,7 @@ Also measured in the same run: the decode workload with wkv as Q2_K blocks
 ("decode_wkv_q2k"), several sequences decoded together ("decode_batched"),
 the prefill workload (T = 4096 Zipf tokens, both layers, one hash pass;
 projection on the MFMA GEMM) under "prefill" with its own roofline, the
-large-table gather workload (6.3 GB Q2_K table, T = 16384 uniform tokens;
+large-table gather workload (5.9 GB Q2_K table, T = 16384 uniform tokens;
 gather + dequant GB/s apart from the GEMM) under "gather_stress", and the
 e4m3 prefill/decode split (four 2048-token calls, then 128 single-token
 steps) under "split_e4m3".
@@ -322,7 +322,7 @@ def bench_prefill(args, torch, E, G, synth):
 
 
 def bench_gather_stress(args, torch, E, G, synth):
-    """The large-table workload (one Q2_K layer of ~75 M rows, 6.3 GB; T
+    """The large-table workload (one Q2_K layer of ~71 M rows, 5.9 GB; T
     16384 uniform tokens, so every row read is a random 84-byte block):
     whole forwards, with the gather + dequant rate reported apart from the
     projection GEMM."""

@@ -244,9 +244,9 @@ def test_forward_split_workload(E):
 
 
 def test_forward_gather_stress(E):
-    """One Q2_K layer over ~75M rows (6.3 GB), T = 16384 uniform tokens."""
+    """One Q2_K layer over ~71M rows (5.9 GB), T = 16384 uniform tokens."""
     w = synth.GATHER_Q2K
-    log("forward: gather stress Q2_K, 75M-row table, T=16384")
+    log("forward: gather stress Q2_K, 71M-row table, T=16384")
     dev = Device(w.name)
     ids = G.token_ids(w)
     T = w.prompt
