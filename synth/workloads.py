@@ -105,8 +105,20 @@ GATHER_Q2K = Workload(
     compressed=100000, p_unmapped=0.15, max_ngram=4, n_heads=8, n_layers=1,
     prime_lo=2**21, prime_hi=2**22, fmt="q2k", token_dist="uniform", prompt=16384)
 
+# edge-case geometry for the tests: an odd number of columns (max_ngram 2, 5
+# heads -> 5 columns, K 1280 = 2.5 KiB rows of bf16: an odd number of 1 KiB
+# loads a row and a partial last 16-value-sub-block round), small tables and
+# hc * dim = 1024; Q2_K and e4m3 tables, and wkv as Q2_K blocks
+ODD_Q2K = Workload(
+    name="odd_cols_q2k_2layer", family=5, vocab=1024, compressed=800, p_unmapped=0.10,
+    max_ngram=2, n_heads=5, n_layers=2, prime_lo=500, prime_hi=1000, fmt="q2k", dim=256,
+    hc=4, token_dist="uniform", prompt=8, decode_steps=24)
+ODD_E4M3 = replace(ODD_Q2K, name="odd_cols_e4m3_2layer", family=6, fmt="e4m3")
+ODD_WKVQ2K = replace(ODD_Q2K, name="odd_cols_q2k_wkvq2k_2layer", wkv_fmt="q2k")
+
 WORKLOADS = {w.name: w for w in (TINY_E4M3, DECODE_Q2K, PREFILL_Q2K, SPLIT_E4M3, GATHER_Q2K,
-                                 DECODE_WKVQ2K)}
+                                 DECODE_WKVQ2K, ODD_Q2K, ODD_E4M3, ODD_WKVQ2K)}
 # seed index of each workload's token / highway stream (tables use `family`)
 STREAM_INDEX = {TINY_E4M3.name: 0, DECODE_Q2K.name: 1, PREFILL_Q2K.name: 2,
-                SPLIT_E4M3.name: 3, GATHER_Q2K.name: 4, DECODE_WKVQ2K.name: 5}
+                SPLIT_E4M3.name: 3, GATHER_Q2K.name: 4, DECODE_WKVQ2K.name: 5,
+                ODD_Q2K.name: 6, ODD_E4M3.name: 7, ODD_WKVQ2K.name: 8}

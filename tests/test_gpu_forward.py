@@ -1,5 +1,6 @@
 """GPU parity of the fused, stateful engram_forward on the five synthetic
-workloads (run on an MI355X).
+workloads, the decode workload with Q2_K wkv and small odd-column edge cases
+(run on an MI355X).
 
 The chain is checked stage by stage on the GPU's own intermediates: hash ids
 (bit for bit against the oracle hasher fed the same token stream), rows (bit
@@ -115,6 +116,37 @@ def test_forward_decode_workload(E):
         assert ctx.position == pos
     ctx.check()
     log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("name", [synth.ODD_Q2K.name, synth.ODD_E4M3.name,
+                                  synth.ODD_WKVQ2K.name])
+def test_forward_odd_columns(E, name):
+    """An odd number of columns (5: K 1280, an odd number of 1 KiB loads a
+    row, a partial last sub-block round): 8-token prompt, then 24
+    single-token steps through the one-launch decode kernels, both layers,
+    every call against the oracle."""
+    dev = Device(name)
+    w = dev.w
+    log(f"forward: {name}, prompt {w.prompt} + {w.decode_steps} steps")
+    ids = G.token_ids(w)
+    max_seq = w.total_tokens
+    ctx = dev.context(max_tokens=w.prompt, max_seq=max_seq)
+    hasher = dev.oracle_hasher(max_seq)
+    d_ids = cuda(ids.astype(np.int32))
+    prompt_h = G.highway(w, w.prompt)
+    step_h = G.highway(w, w.decode_steps, decode=True)
+    pos = 0
+    for step in range(1 + w.decode_steps):
+        T = w.prompt if step == 0 else 1
+        h0 = prompt_h if step == 0 else step_h[step - 1:step]
+        want_ids = hasher.hash(ids[pos:pos + T], pos)
+        for layer in range(w.n_layers):
+            d_h = torch.from_numpy(h0).cuda()
+            ctx.forward(layer, d_ids[pos:pos + T] if layer == 0 else None, T, d_h)
+            check_call(dev, ctx, layer, ids[pos:pos + T], want_ids, h0, d_h.cpu().numpy(), T,
+                       label=f"step {step} layer {layer}")
+        pos += T
+    ctx.check()
 
 
 def test_forward_decode_wkv_q2k(E):
@@ -308,7 +340,8 @@ def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
 
 
 @pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name,
-                                  synth.DECODE_WKVQ2K.name])
+                                  synth.DECODE_WKVQ2K.name, synth.ODD_Q2K.name,
+                                  synth.ODD_E4M3.name, synth.ODD_WKVQ2K.name])
 def test_fused_decode_matches_staged(E, name):
     """The one-launch decode layer (hash + gather + projection) leaves exactly
     what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""
@@ -334,12 +367,13 @@ def test_fused_decode_matches_staged(E, name):
     np.testing.assert_array_equal(calls[-1][0], want[-1:])
 
 
-def test_wkv_q2k_forward_matches_bf16_expansion(E):
-    """The decode workload with Q2_K wkv: every step through the kernels over
-    the blocks (one launch or staged) leaves exactly what the bf16 kernels
-    over the expanded wkv leave (row ids, rows, kv, highway) -- the pages'
+@pytest.mark.parametrize("name", [synth.DECODE_WKVQ2K.name, synth.ODD_WKVQ2K.name])
+def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
+    """Workloads with Q2_K wkv: every step through the kernels over the
+    blocks (one launch or staged) leaves exactly what the bf16 kernels over
+    the expanded wkv leave (row ids, rows, kv, highway) -- the pages'
     byte-identical results."""
-    dev = Device(synth.DECODE_WKVQ2K.name)
+    dev = Device(name)
     w = dev.w
     prompt, steps = 8, 24
     log(f"Q2_K wkv vs bf16 expansion: {w.name}, prompt {prompt} + {steps} steps")
