@@ -145,6 +145,8 @@ int32_t dispatch_project(const uint16_t *x, const uint16_t *w, uint16_t *y, int6
         return ENGRAM_OK;
     if (T == 1 && K <= kGemvMaxK)
         return launch_gemv(x, w, y, T, K, N, l);
+    if (gemv_multi_fits(T, K))
+        return launch_gemv_multi(x, w, y, T, K, N, l);
     if (gemm_small_fits(T, K, N))
         return launch_gemm_small(x, w, y, T, K, N, l);
     if (T <= kGemvMaxT && K <= kGemvMaxK)

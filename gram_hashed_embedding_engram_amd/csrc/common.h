@@ -139,6 +139,17 @@ __device__ __forceinline__ void subblock_dot(const u32x4 &wa, const u32x4 &wb, c
     acc2 = dot2(wb.w, xb.w, acc2);
 }
 
+// Activations kept in LDS for the one-token order: chunk c (8 values) sits at
+// slot xslot(c), so lane l's chunks 2g and 2g+1 of sub-block g = 64s + l are
+// at 128s + l and 128s + 64 + l -- a wavefront's reads of either are 64
+// consecutive 16-byte slots, free of bank conflicts (in chunk order they
+// would be 32 bytes apart).  A buffer of kc chunks needs kc rounded up to a
+// multiple of 128 slots.
+__device__ __forceinline__ int xslot(int c)
+{
+    return (c & ~127) + ((c & 1) << 6) + ((c & 127) >> 1);
+}
+
 // A bf16 row read as NI coalesced 1 KiB loads (lane l holds chunk 64m + l of
 // load m) is brought into sub-block order through the wavefront's own 2 KiB
 // LDS buffer `stage`, one 128-chunk segment (loads 2s, 2s+1) at a time:
@@ -272,5 +283,13 @@ int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int
 // GEMV covers T <= kGemvMaxT with K <= kGemvMaxK; larger T goes to the GEMM.
 constexpr int64_t kGemvMaxT = 4;
 constexpr int64_t kGemvMaxK = 8192;
+// The multi-token GEMV (2..kGemvMultiMaxT tokens in one pass, activations in
+// LDS: T*K <= kGemvMultiMaxX values, 96 KiB).  From 5 tokens the MFMA weight
+// stream is faster (and the GEMV's registers spill from 6).
+constexpr int64_t kGemvMultiMaxT = 4;
+constexpr int64_t kGemvMultiMaxX = 49152;   // values: T * (K rounded up to 1024)
+bool gemv_multi_fits(int64_t T, int64_t K);
+int32_t launch_gemv_multi(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t T,
+                          int64_t K, int64_t N, const Launch &l);
 
 }  // namespace engram

@@ -101,7 +101,7 @@ __device__ __forceinline__ SlotConsts slot_consts(const HashConsts &c)
 // Hash of the token and gather + dequant of this layer's cols rows into the
 // activations s_x by the NT threads of a workgroup (every workgroup;
 // workgroup 0 also writes the row ids, the history entry and the dequantised
-// rows).  Ends with s_x complete.  The token, its look-back and (Q2_K) the
+// rows).  Ends with s_x complete, chunk c at slot xslot(c).  The token, its look-back and (Q2_K) the
 // table blocks come through the scalar cache, so nothing here waits for the
 // weight loads the kernel has in flight.
 template <int FMT, int NT>
@@ -212,7 +212,7 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
         __syncthreads();
         for (int ch = tid; ch < kc; ch += NT) {
             const int r = ch >> 5;
-            s_x[ch] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
+            s_x[xslot(ch)] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
         }
     } else {
         const int nb = 256 / a.scale_block;
@@ -224,13 +224,13 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
                 const uint32_t *b = (const uint32_t *)(a.table + id * 256 + 8 * sub);
                 o = e4m3_dequant8(b[0], b[1], a.scales[id * nb + (8 * sub) / a.scale_block]);
             }
-            s_x[ch] = o;
+            s_x[xslot(ch)] = o;
         }
     }
     __syncthreads();
     if (blockIdx.x == 0)
         for (int ch = tid; ch < kc; ch += NT)
-            ((u32x4 *)a.rows)[ch] = s_x[ch];
+            ((u32x4 *)a.rows)[ch] = s_x[xslot(ch)];
 }
 
 template <int FMT, int NI>
@@ -281,8 +281,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
         float acc = 0.0f, acc2 = 0.0f;
         for_each_subblock<NI>(wv, s_stage[tid >> 6], lane, n_sb,
                               [&](int s, const u32x4 &wa, const u32x4 &wb) {
-                                  const int g = 64 * s + lane;
-                                  subblock_dot(wa, wb, s_x[2 * g], s_x[2 * g + 1], acc, acc2);
+                                  subblock_dot(wa, wb, s_x[128 * s + lane],
+                                               s_x[128 * s + 64 + lane], acc, acc2);
                               });
         prev_v = f32_to_bf16(wave_sum(acc + acc2));
         prev_n = n;

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kQ2kThreads, 8) void gemv_q2k_kernel(const uint16_t
 
     // the token's activations, once per workgroup, into LDS
     for (int ch = tid; ch < (K >> 3); ch += kQ2kThreads)
-        s_x[ch] = ((const u32x4 *)x)[ch];
+        s_x[xslot(ch)] = ((const u32x4 *)x)[ch];
     __syncthreads();
 
     for (int64_t n = wave; n < N; n += n_waves) {

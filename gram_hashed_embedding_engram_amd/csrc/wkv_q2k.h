@@ -60,8 +60,8 @@ __device__ __forceinline__ void q2k_row_stage(uint32_t *lds, const uint32_t (&r)
 // The row's dot product with the activations, this lane's share: sub-blocks
 // g = lane + 64*i < n_sb (n_sb = K/16, so only the last round, i = NSB-1,
 // can leave lanes idle).  xs = the token's activations in LDS as 8-value
-// chunks (chunks 2g, 2g+1 belong to sub-block g); lds = the row's blocks, 21
-// dwords each.  The order is the one-token projection order of common.h
+// chunks, chunk c at slot xslot(c) (chunks 2g, 2g+1 belong to sub-block g);
+// lds = the row's blocks, 21 dwords each.  The order is the one-token projection order of common.h
 // (pairs 0, 2, 4, 6 of a sub-block into acc, 1, 3, 5, 7 into acc2), so the
 // result equals the bf16 GEMV's over the expanded weights bit for bit.
 template <int NSB>
@@ -94,7 +94,7 @@ __device__ __forceinline__ float q2k_row_dot(const uint32_t *lds, const u32x4 *x
         // bit 2*((sb>>1)&3) -- four dwords of quants, one shift
         const uint32_t *q = blk + 4 + 8 * (sb >> 3) + 4 * (sb & 1);
         const int shift = 2 * ((sb >> 1) & 3);
-        const u32x4 xa = xs[2 * g], xb = xs[2 * g + 1];
+        const u32x4 xa = xs[128 * i + lane], xb = xs[128 * i + 64 + lane];   // xslot(2g), xslot(2g+1)
         const uint32_t x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
         for (int j = 0; j < 4; j++) {

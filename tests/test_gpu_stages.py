@@ -256,13 +256,39 @@ def test_project_gemv_decode_shape(E, decode, T):
 @pytest.mark.parametrize("M", [2, 5, 16, 17, 33, 64])
 def test_project_small_decode_shape(E, decode, M):
     """A few tokens (several sequences' decode tokens, short prompts) through
-    the decode-shape wkv: the MFMA GEMM laid out as a weight stream, every
-    output checked (partial token tiles at M = 5, 17, 33)."""
+    the decode-shape wkv: the multi-token GEMV (M <= 8) or the MFMA GEMM laid
+    out as a weight stream, every output checked (partial token tiles at
+    M = 17, 33)."""
     rng = np.random.default_rng(100 + M)
     ids = rng.integers(0, decode.layers[0]["rows"], size=(M, 24))
     x = decode.oracle_rows(0, ids).reshape(M, -1)
     log(f"project small: M={M} K=6144 N=20480")
     check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
+
+
+@pytest.mark.parametrize("T,K,N", [(2, 6144, 20480), (4, 6144, 20480), (3, 1280, 1008),
+                                   (4, 8192, 2064), (2, 512, 16), (3, 1088, 4000)])
+def test_project_multi_token_equals_one_token(E, T, K, N):
+    """2..4 tokens in one pass over the weights: each token's outputs equal
+    a one-token call's bit for bit (same summation order), and the oracle's
+    within the projection tolerance.  K from one 1 KiB load a row to 8192 (and
+    one not a multiple of 1024), N not a multiple of the 16 wavefronts of a
+    workgroup."""
+    import oracle
+    rng = np.random.default_rng(1000 + 7 * T + K)
+    x = bf16_rand(rng, (T, K), 1.0)
+    w = bf16_rand(rng, (N, K), 0.02)
+    d_w = cuda(w)
+    y = torch.empty(T, N, dtype=torch.int16, device="cuda")
+    log(f"project multi-token: T={T} K={K} N={N}")
+    E.project(cuda(x), d_w, y)
+    got = to_np_u16(y)
+    for t in range(T):
+        y1 = torch.empty(1, N, dtype=torch.int16, device="cuda")
+        E.project(cuda(x[t:t + 1]), d_w, y1)
+        np.testing.assert_array_equal(got[t], to_np_u16(y1)[0], err_msg=f"token {t}")
+    want = oracle.linear_bf16(x, w)
+    assert relerr(widen(got), widen(want)) <= 1e-2
 
 
 @pytest.mark.parametrize("M", [2, 5, 64, 255, 257, 300, 513])
