@@ -167,9 +167,10 @@ int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_id
 /* y[t][n] = bf16( sum_k x[t][k] * w[n][k] ) with f32 accumulation
  * (metrale "engram.rs", linear_bf16; atlascybernetics "engram_v41.rs",
  * module doc stage 3: [tokens, cols*head_dim] x wkv^T -> [tokens,
- * dim*(hc+1)]).  A bandwidth-bound GEMV serves T = 1, an MFMA GEMM laid out as
- * a weight stream 2 <= T <= 64 (K a multiple of 1024), the tiled MFMA GEMM
- * larger T (and the GEMV T <= 4 for other K).
+ * dim*(hc+1)]).  A bandwidth-bound GEMV serves T = 1 and 2 <= T <= 4 (the
+ * tokens in one pass over the weights; each token's outputs then equal those
+ * of a one-token call bit for bit), an MFMA GEMM laid out as a weight stream
+ * 5 <= T <= 64 (K a multiple of 1024), the tiled MFMA GEMM larger T.
  *   d_x [T][K], d_w [N][K], d_y [T][N], all bf16; K a multiple of 64. */
 int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
                        int64_t K, int64_t N, void *stream);
