@@ -584,6 +584,28 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
             return launch_gate(d_h, ctx->kv, L.qk, 1, cfg.hc, cfg.dim, cfg.eps, l);
         });
     }
+    // one decode token of each of 2..4 sequences: the same, all tokens in one
+    // pass over the weights
+    if (T == 1 && B >= 2 && B <= kDecodeMultiMaxB && ctx->fused_decode && !L.wkv_q2k &&
+        cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols && ctx->nl * ctx->cols <= 64) {
+        if (hash_index == 0) {
+            ctx->step_start = ctx->pos;
+            ctx->pos += 1;
+            ctx->step_open = true;
+            ctx->step_T = 1;
+        }
+        rc = staged(ctx, 2, s, [&](const Launch &l) {
+            return launch_decode_multi(ctx->consts, cfg.hash.d_token_map, d_ids, ctx->step_start,
+                                       ctx->history, cfg.max_seq, hash_index, hash_index == 0,
+                                       L.tab, L.wkv, ctx->kv, ctx->kv_width, ctx->row_ids,
+                                       ctx->rows, ctx->err, B, l);
+        });
+        if (rc != ENGRAM_OK)
+            return rc;
+        return staged(ctx, 3, s, [&](const Launch &l) {
+            return launch_gate(d_h, ctx->kv, L.qk, M, cfg.hc, cfg.dim, cfg.eps, l);
+        });
+    }
     if (hash_index == 0) {
         const int64_t start = ctx->pos;
         rc = staged(ctx, 0, s, [&](const Launch &l) {

@@ -263,6 +263,14 @@ int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
 // read back from history[pos].  rows [cols*256] receives the dequantised rows.
 // w_q2k non-null: the projection reads wkv's Q2_K blocks [N][K/256][84]
 // instead of the bf16 w.
+// The one-launch decode step of B = 2..kDecodeMultiMaxB sequences at one
+// position (history [B][hist_stride]); bf16 wkv; n_layers*cols <= 64.
+constexpr int64_t kDecodeMultiMaxB = 4;
+int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
+                            int64_t pos, int64_t *history, int64_t hist_stride, int32_t layer,
+                            bool first_layer, const engram_table &tab, const uint16_t *w,
+                            uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows,
+                            int32_t *err, int64_t B, const Launch &l);
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
                       int64_t pos, int64_t *history, int32_t layer, bool first_layer,
                       const engram_table &tab, const uint16_t *w, const uint8_t *w_q2k,

@@ -56,6 +56,7 @@ struct DecodeArgs {
     int64_t *row_ids;
     uint16_t *rows;
     int32_t *err;
+    int64_t hist_stride;     // history entries per sequence (several sequences)
 };
 
 // A load of a value that no thread writes during the launch, through the
@@ -333,7 +334,256 @@ __global__ __launch_bounds__(kQ2kwThreads, 8) void decode_q2kw_kernel(const Hash
     }
 }
 
+// The same decode step for NB = 2..4 sequences that advance together (one
+// token each, all at position a.pos, sequence b's history at history +
+// b*hist_stride): one launch hashes, gathers and dequantises the NB tokens
+// and projects them in one pass over wkv, every token in the one-token order
+// (its kv equals a one-sequence step's bit for bit).  One 1024-thread
+// workgroup per CU.  Wavefront b < NB hashes sequence b -- lane = slot (layer
+// lane / cols, column lane % cols), so at most 64 slots -- with the token,
+// its look-back and the hash constants as scalar loads (no vector load waits
+// behind the weight row in flight).  All 16 wavefronts then stage the NB*cols
+// Q2_K blocks through the scalar cache, and the workgroup expands them into
+// the NB tokens' activations in LDS.
+constexpr int kDecodeMultiThreads = 1024;
+
+template <int FMT, int NB, int NI>
+__global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
+    const HashConsts c, const DecodeArgs a, const uint16_t *__restrict__ w)
+{
+    constexpr int NW = kDecodeMultiThreads / 64;
+    __shared__ int64_t s_id[NB * kDecodeMaxCols];
+    __shared__ uint32_t s_blk[NB * kDecodeMaxCols * 21];
+    __shared__ u32x4 s_x[NB * kMaxChunks];
+    __shared__ u32x4 s_stage[NW][128];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cols = c.cols, nslots = c.nl * cols;
+    const int64_t K = (int64_t)cols * 256, N = a.N;
+    const int kc = cols * 32, kcp = (kc + 127) & ~127, n_sb = cols * 16;
+    const int64_t wave = (int64_t)blockIdx.x * NW + wid;
+    const int64_t n_waves = (int64_t)gridDim.x * NW;
+    const int64_t pos = a.pos;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // ---- the first wkv row of this wavefront (past the row's end: its last
+    // chunk again)
+    const int slot = min(lane, nslots - 1);
+    const u32x4 *wr0 = (const u32x4 *)(w + min(wave, N - 1) * K);
+    u32x4 wv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++)
+        wv[i] = __builtin_nontemporal_load(wr0 + min(i * 64 + lane, kc - 1));
+
+    // ---- hash of sequence b = wid
+    if (wid < NB) {
+        const int b = wid;
+        int64_t *hist = a.history + (int64_t)b * a.hist_stride;
+        int64_t win[ENGRAM_MAX_NGRAM];
+        bool bad = false;
+        if (a.first_layer) {
+            const int32_t t = cload(a.ids + b);
+            bad = t < 0 || (int64_t)t >= c.vocab;
+            const int64_t mapped = cload(a.token_map + (bad ? 0 : t));
+            win[0] = bad ? -1 : mapped;          // reported, then hashed as unmapped
+        } else {
+            win[0] = cload(hist + pos);
+        }
+#pragma unroll
+        for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
+            win[k] = -1;
+            if (k < c.ng) {
+                const int64_t q = pos - k;
+                const int64_t v = cload(hist + (q >= 0 ? q : 0));
+                win[k] = q >= 0 ? v : -1;
+            }
+        }
+        const int l = slot / cols, col = slot - l * cols;
+        // slot i's prime and offset into lane i: scalar loads of the kernel
+        // arguments moved into lanes (v_writelane), no vector loads
+        uint32_t p_lo = 1u, p_hi = 0u, o_lo = 0u, o_hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 64; i++) {
+            if (i < nslots) {
+                const uint64_t pi = (uint64_t)c.prime[i], oi = (uint64_t)c.offset[i];
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(p_lo) : "s"((uint32_t)pi), "i"(i));
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(p_hi) : "s"((uint32_t)(pi >> 32)), "i"(i));
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(o_lo) : "s"((uint32_t)oi), "i"(i));
+                asm("v_writelane_b32 %0, %1, %2" : "+v"(o_hi) : "s"((uint32_t)(oi >> 32)), "i"(i));
+            }
+        }
+        const int64_t prime = (int64_t)(((uint64_t)p_hi << 32) | p_lo);
+        const int64_t offset = (int64_t)(((uint64_t)o_hi << 32) | o_lo);
+        int64_t m[ENGRAM_MAX_NGRAM];
+#pragma unroll
+        for (int k = 0; k < ENGRAM_MAX_NGRAM; k++)
+            m[k] = 0;
+        for (int ll = 0; ll < c.nl; ll++)
+#pragma unroll
+            for (int k = 0; k < ENGRAM_MAX_NGRAM; k++) {
+                const int64_t mk = k < c.ng ? c.mult[ll * c.ng + k] : 0;
+                m[k] = l == ll ? mk : m[k];
+            }
+        if (lane < nslots && (l == a.layer || (blockIdx.x == 0 && a.first_layer))) {
+            const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
+            bool blocked = win[0] == -1;
+            uint64_t r = (uint64_t)(blocked ? c.pad_id : win[0]) * (uint64_t)m[0];
+#pragma unroll
+            for (int k = 1; k < ENGRAM_MAX_NGRAM; k++) {
+                if (k < ngram) {
+                    blocked = blocked || win[k] == -1;
+                    r ^= (uint64_t)(blocked ? c.pad_id : win[k]) * (uint64_t)m[k];
+                }
+            }
+            const int64_t id = rem_euclid((int64_t)r, prime) + offset;
+            if (blockIdx.x == 0) {
+                a.row_ids[(int64_t)b * nslots + slot] = id;
+                if (lane == 0 && a.first_layer) {
+                    hist[pos] = win[0];
+                    if (bad && a.err)
+                        atomicOr(a.err, ENGRAM_DEVERR_TOKEN);
+                }
+            }
+            if (l == a.layer) {
+                const bool in_table = id >= 0 && id < a.n_rows;
+                if (!in_table && blockIdx.x == 0 && a.err)
+                    atomicOr(a.err, ENGRAM_DEVERR_ROW);
+                s_id[b * cols + col] = in_table ? id : -1;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gather + dequant of the NB*cols rows into the activations
+    const int nrows = NB * cols;
+    if (FMT == ENGRAM_FMT_Q2K) {
+        constexpr int kBatch = 2;      // 42 SGPRs of blocks a round trip
+        for (int r0 = wid; r0 < nrows; r0 += kBatch * NW) {
+            int64_t id[kBatch];
+            const uint32_t *blk[kBatch];
+#pragma unroll
+            for (int bb = 0; bb < kBatch; bb++) {
+                const int r = r0 + bb * NW;
+                id[bb] = r < nrows ? uniform64(s_id[r]) : -1;
+                blk[bb] = (const uint32_t *)(a.table + (id[bb] >= 0 ? id[bb] : 0) *
+                                                           ENGRAM_Q2K_ROW_BYTES);
+            }
+            uint32_t d[kBatch][21];
+#pragma unroll
+            for (int bb = 0; bb < kBatch; bb++)
+#pragma unroll
+                for (int j = 0; j < 21; j++)
+                    d[bb][j] = cload(blk[bb] + j);
+#pragma unroll
+            for (int bb = 0; bb < kBatch; bb++) {
+                uint32_t v = 0u;
+#pragma unroll
+                for (int j = 0; j < 21; j++)      // dword j into lane j (v_writelane)
+                    asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(d[bb][j]), "i"(j));
+                const int r = r0 + bb * NW;
+                if (r < nrows && lane < 21)
+                    s_blk[r * 21 + lane] = id[bb] >= 0 ? v : 0u;
+            }
+        }
+        __syncthreads();
+        for (int ch = tid; ch < NB * kc; ch += kDecodeMultiThreads) {
+            const int b = ch / kc, chl = ch - b * kc, r = b * cols + (chl >> 5);
+            s_x[b * kcp + xslot(chl)] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, chl & 31) : zero;
+        }
+    } else {
+        const int nb = 256 / a.scale_block;
+        for (int ch = tid; ch < NB * kc; ch += kDecodeMultiThreads) {
+            const int b = ch / kc, chl = ch - b * kc, sub = chl & 31;
+            const int64_t id = s_id[b * cols + (chl >> 5)];
+            u32x4 o = zero;
+            if (id >= 0) {
+                const uint32_t *p = (const uint32_t *)(a.table + id * 256 + 8 * sub);
+                o = e4m3_dequant8(p[0], p[1], a.scales[id * nb + (8 * sub) / a.scale_block]);
+            }
+            s_x[b * kcp + xslot(chl)] = o;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int ch = tid; ch < NB * kc; ch += kDecodeMultiThreads) {
+            const int b = ch / kc, chl = ch - b * kc;
+            ((u32x4 *)a.rows)[(int64_t)b * kc + chl] = s_x[b * kcp + xslot(chl)];
+        }
+
+    // ---- projection: rows wave, wave + n_waves, ..., all NB tokens at once
+    u32x4 *stage = s_stage[wid];
+    for (int64_t n = wave; n < N; n += n_waves) {
+        if (n != wave) {
+            const u32x4 *wr = (const u32x4 *)(w + n * K);
+#pragma unroll
+            for (int i = 0; i < NI; i++)
+                wv[i] = __builtin_nontemporal_load(wr + min(i * 64 + lane, kc - 1));
+        }
+        float acc[NB], acc2[NB];
+#pragma unroll
+        for (int t = 0; t < NB; t++)
+            acc[t] = acc2[t] = 0.0f;
+        for_each_subblock<NI>(wv, stage, lane, n_sb, [&](int s, const u32x4 &wa, const u32x4 &wb) {
+#pragma unroll
+            for (int t = 0; t < NB; t++)
+                subblock_dot(wa, wb, s_x[t * kcp + 128 * s + lane],
+                             s_x[t * kcp + 128 * s + 64 + lane], acc[t], acc2[t]);
+        });
+#pragma unroll
+        for (int t = 0; t < NB; t++) {
+            const float v = wave_sum(acc[t] + acc2[t]);
+            if (lane == t)
+                a.y[t * N + n] = f32_to_bf16(v);
+        }
+    }
+}
+
 }  // namespace
+
+int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
+                            int64_t pos, int64_t *history, int64_t hist_stride, int32_t layer,
+                            bool first_layer, const engram_table &tab, const uint16_t *w,
+                            uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows,
+                            int32_t *err, int64_t B, const Launch &l)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
+                       tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
+                       row_ids, rows, err, hist_stride};
+    const int ni = (c.cols * 256 + 511) / 512;
+    int64_t blocks = (N + 15) / 16;
+    if (blocks > cus)
+        blocks = cus;
+    const dim3 grid((unsigned)blocks), block(kDecodeMultiThreads);
+    const bool q2k = tab.fmt == ENGRAM_FMT_Q2K;
+#define ENGRAM_DM_CASE(B_, NI_)                                                                  \
+    if (B == B_ && ni == NI_) {                                                                  \
+        if (q2k)                                                                                 \
+            dispatch(decode_multi_kernel<ENGRAM_FMT_Q2K, B_, NI_>, grid, block, l, true, true, c, \
+                     a, w);                                                                      \
+        else                                                                                     \
+            dispatch(decode_multi_kernel<ENGRAM_FMT_E4M3, B_, NI_>, grid, block, l, true, true,   \
+                     c, a, w);                                                                   \
+        return launch_status("engram decode kernel");                                           \
+    }
+#define ENGRAM_DM_ROW(B_)                                                                        \
+    ENGRAM_DM_CASE(B_, 1) ENGRAM_DM_CASE(B_, 2) ENGRAM_DM_CASE(B_, 3) ENGRAM_DM_CASE(B_, 4)      \
+    ENGRAM_DM_CASE(B_, 5) ENGRAM_DM_CASE(B_, 6) ENGRAM_DM_CASE(B_, 7) ENGRAM_DM_CASE(B_, 8)      \
+    ENGRAM_DM_CASE(B_, 9) ENGRAM_DM_CASE(B_, 10) ENGRAM_DM_CASE(B_, 11) ENGRAM_DM_CASE(B_, 12)   \
+    ENGRAM_DM_CASE(B_, 13) ENGRAM_DM_CASE(B_, 14) ENGRAM_DM_CASE(B_, 15) ENGRAM_DM_CASE(B_, 16)
+    ENGRAM_DM_ROW(2) ENGRAM_DM_ROW(3) ENGRAM_DM_ROW(4)
+#undef ENGRAM_DM_ROW
+#undef ENGRAM_DM_CASE
+    return fail(ENGRAM_E_UNSUPPORTED, "engram decode: %lld sequences, %d columns", (long long)B,
+                c.cols);
+}
 
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
                       int64_t pos, int64_t *history, int32_t layer, bool first_layer,
@@ -351,7 +601,7 @@ int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32
     }
     const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
                        tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
-                       row_ids, rows, err};
+                       row_ids, rows, err, 0};
     const int64_t K = (int64_t)c.cols * 256;
     int64_t blocks = (N + 3) / 4;
     const int64_t cap = (int64_t)cus * kDecodeBlocksPerCu;

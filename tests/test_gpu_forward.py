@@ -396,6 +396,61 @@ def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
                 np.testing.assert_array_equal(x, y, err_msg=f"call {i}: {what}")
 
 
+@pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 2), (synth.DECODE_Q2K.name, 3),
+                                    (synth.DECODE_Q2K.name, 4), (synth.ODD_Q2K.name, 3),
+                                    (synth.ODD_E4M3.name, 4)])
+def test_fused_batched_decode_matches_staged(E, name, B):
+    """B sequences' decode steps through the one-launch several-sequence
+    kernel leave exactly what the staged kernels leave (row ids, rows, kv,
+    highway, bit for bit), and each sequence's kv equals a one-sequence run's
+    (the projection adds in the one-token order)."""
+    dev = Device(name)
+    w = dev.w
+    prompt, steps = 4, 12
+    log(f"fused vs staged batched decode: {name}, B={B}")
+    ids = G.token_ids(w, B * (prompt + steps)).reshape(B, prompt + steps)
+    hp = G.highway(w, B * prompt).reshape(B, prompt, w.hc, w.dim)
+    hs = G.highway(w, B * steps).reshape(steps, B, w.hc, w.dim)
+    res = []
+    for fused in (True, False):
+        ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps, batch=B)
+        ctx.set_fused_decode(fused)
+        d_ids = cuda(ids.astype(np.int32))
+        out = []
+        for step in range(1 + steps):
+            T = prompt if step == 0 else 1
+            p0 = 0 if step == 0 else prompt + step - 1
+            h0 = hp if step == 0 else hs[step - 1][:, None]
+            for layer in range(w.n_layers):
+                d_h = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
+                ctx.forward(layer, d_ids[:, p0:p0 + T].contiguous() if layer == 0 else None, T, d_h)
+                rid, rows, kv = ctx.views(T)
+                out.append((rid.cpu().numpy(), to_np_u16(rows), to_np_u16(kv),
+                            d_h.cpu().numpy().view(np.uint32)))
+        ctx.check()
+        res.append(out)
+    for i, (a, b) in enumerate(zip(*res)):
+        for x, y, what in zip(a, b, ("row ids", "rows", "kv", "highway")):
+            np.testing.assert_array_equal(x, y, err_msg=f"call {i}: {what}")
+    # one sequence alone (batch 1) gives the same kv for that sequence
+    ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps)
+    d_ids = cuda(ids[B - 1].astype(np.int32))
+    k = 0
+    for step in range(1 + steps):
+        T = prompt if step == 0 else 1
+        p0 = 0 if step == 0 else prompt + step - 1
+        h0 = hp[B - 1] if step == 0 else hs[step - 1][B - 1:B]
+        for layer in range(w.n_layers):
+            d_h = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
+            ctx.forward(layer, d_ids[p0:p0 + T] if layer == 0 else None, T, d_h)
+            if step > 0:
+                _, _, kv1 = ctx.views(T)
+                np.testing.assert_array_equal(to_np_u16(kv1)[0], res[0][k][2][B - 1],
+                                              err_msg=f"step {step} layer {layer}")
+            k += 1
+    ctx.check()
+
+
 def test_fused_decode_bad_token(E):
     w = synth.TINY_E4M3
     dev = Device(w.name)
