@@ -113,6 +113,20 @@ def device_inputs(w, torch, E, G):
     return ht, tm, tables, layers, host
 
 
+def host_table_inputs(w, inputs, torch, E):
+    """The same inputs with every layer's table (and e4m3 scales) moved to
+    pinned host memory, read by the kernels across the host link; wkv, qk
+    and the hash tables stay on the device."""
+    ht, tm, tables, layers, host = inputs
+    out = []
+    for (tab, *rest), L in zip(layers, host):
+        data = torch.from_numpy(L["table"]).pin_memory()
+        scales = None if L["scales"] is None else torch.from_numpy(L["scales"]).pin_memory()
+        out.append((E.Table(data, scales, head_dim=w.head_dim, scale_block=w.scale_block),
+                    *rest))
+    return ht, tm, tables, out, host
+
+
 def make_ctx(E, w, tables, layers, max_tokens, max_seq, batch=1):
     ctx = E.Context(tables, w.hc, w.dim, w.head_dim, w.eps, max_tokens, max_seq, batch=batch)
     for l, layer in enumerate(layers):
@@ -328,43 +342,48 @@ def bench_gather_stress(args, torch, E, G, synth):
     projection GEMM."""
     w = synth.GATHER_Q2K
     log(f"gather stress: generating {w.name}")
-    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
-    del host
+    inputs = device_inputs(w, torch, E, G)
+    ht, tm, tables, layers, host = inputs
     T = w.prompt
     reps, warm = args.stress_steps, 1
     ids = G.token_ids(w)
     d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
     h = torch.from_numpy(G.highway(w, T)).cuda()
-    ctx = make_ctx(E, w, tables, layers, T, T * (warm + 2 * reps))
     stream = torch.cuda.current_stream()
 
-    def step():
-        for l in range(w.n_layers):
-            ctx.forward(l, d_ids, T, h)
+    def run(layers):
+        ctx = make_ctx(E, w, tables, layers, T, T * (warm + 2 * reps))
 
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ctx.set_timing(True)
-    for _ in range(reps):
-        step()
-    torch.cuda.synchronize()
-    stages = ctx.timing()
-    ctx.check()
-    avg = {k: v[0] / max(1, v[1]) for k, v in stages.items()}
+        def step():
+            for l in range(w.n_layers):
+                ctx.forward(l, d_ids, T, h)
+
+        for _ in range(warm):
+            step()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        ctx.set_timing(True)
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        stages = ctx.timing()
+        ctx.check()
+        del ctx
+        return ms, {k: v[0] / max(1, v[1]) for k, v in stages.items()}
+
     gather_bytes = T * w.cols * (8 + 84 + w.head_dim * 2)
+    ms, avg = run(layers)
     gbps = gather_bytes / (avg["gather"] / 1e3) / 1e9
     tflops = 2.0 * T * w.K * w.N / (avg["project"] / 1e3) / 1e12
     rows = int(ht["offsets"][0][-1] + ht["primes"][0][-1])
-    del ctx
-    return dict(
+    res = dict(
         workload=w.name, T=T, layers=w.n_layers, table_rows=rows, table_bytes=rows * 84,
         ms_per_step=ms / reps, value=reps * T * w.n_layers / (ms / 1e3),
         unit="engram tokens/s per layer", stages_ms=avg,
@@ -374,6 +393,19 @@ def bench_gather_stress(args, torch, E, G, synth):
                     traffic=counter_traffic("gather_stress_counters.md", "gather.hip")),
         project=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                      frac=tflops / BF16_PEAK_TFLOPS))
+    if args.host_tables:
+        # the same forwards with the 5.9 GB table in pinned host memory: the
+        # gather's 84-byte row reads cross the host link
+        del layers
+        hinputs = host_table_inputs(w, inputs, torch, E)
+        del inputs
+        torch.cuda.empty_cache()
+        ms_h, avg_h = run(hinputs[3])
+        res["host_table"] = dict(
+            ms_per_step=ms_h / reps, value=reps * T * w.n_layers / (ms_h / 1e3),
+            stages_ms=avg_h, gather_table_GBps=T * w.cols * 84 / (avg_h["gather"] / 1e3) / 1e9,
+            gather_GBps=gather_bytes / (avg_h["gather"] / 1e3) / 1e9)
+    return res
 
 
 def bench_split(args, torch, E, G, synth):
@@ -474,6 +506,10 @@ def main():
     ap.add_argument("--split-passes", type=int, default=2)
     ap.add_argument("--only-stress", action="store_true",
                     help="run only the gather-stress measurement (for counter passes)")
+    ap.add_argument("--host-tables", action="store_true",
+                    help="also time decode and the gather stress with the tables in pinned "
+                         "host memory (off by default: its launches of the same kernels would "
+                         "mix into a kernel trace of the default run)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy of BYTES bytes (read BYTES, write "
                          "BYTES) three times: the calibration kernel for the HBM counters")
@@ -516,6 +552,13 @@ def main():
     staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=inputs)
     log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
         f"{staged['stages']}")
+    host_dec = None
+    if args.host_tables:
+        hinputs = host_table_inputs(synth.DECODE_Q2K, inputs, torch, E)
+        host_dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=hinputs)
+        log(f"decode (host tables): {host_dec['ms_per_step'] * 1e3:.1f} us/step, "
+            f"stages(ms) {host_dec['stages']}")
+        del hinputs
     batched = []
     for B in args.batch_sequences:
         r = bench_decode_batched(args, torch, E, G, synth, inputs, B)
@@ -590,6 +633,11 @@ def main():
             "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
             "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
                        "stages_ms_per_layer_step": decq_staged["stages"]}},
+        "decode_host_tables": None if host_dec is None else {
+            "tables": "pinned host memory, rows read across the host link",
+            "ms_per_step": host_dec["ms_per_step"], "value": host_dec["value"],
+            "unit": "engram tokens/s per layer",
+            "stages_ms_per_layer_step": host_dec["stages"]},
         "decode_batched": batched,
         "prefill": pre,
         "gather_stress": stress,

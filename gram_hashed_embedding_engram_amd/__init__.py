@@ -30,7 +30,7 @@ EXPORTS = (
     "engram_forward",
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
-    "engram_ctx_timing", "engram_ctx_destroy",
+    "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host",
 )
 
 
@@ -98,6 +98,7 @@ def lib():
             "engram_ctx_set_timing": (i32, [p, i32]),
             "engram_ctx_timing": (i32, [p, p, p]),
             "engram_ctx_destroy": (None, [p]),
+            "engram_map_host": (i32, [p, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -152,16 +153,30 @@ class HashTables:
                              self.offsets.ctypes.data)
 
 
+def map_host(t):
+    """Device address of a pinned host tensor (engram_map_host)."""
+    dev = ctypes.c_void_p()
+    _check(lib().engram_map_host(ctypes.c_void_p(t.data_ptr()), ctypes.byref(dev)))
+    return dev.value
+
+
+def _table_ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr() if t.is_cuda else map_host(t)
+
+
 class Table:
-    """One layer's device-resident table (Q2_K blocks, or e4m3 codes with
-    f32 block scales)."""
+    """One layer's table (Q2_K blocks, or e4m3 codes with f32 block scales),
+    as device tensors or as pinned host tensors the kernels read across the
+    host link."""
 
     def __init__(self, d_data, d_scales=None, head_dim=256, scale_block=128):
         fmt = FMT_Q2K if d_scales is None else FMT_E4M3
         n_rows = int(d_data.shape[0])
         self.data, self.scales = d_data, d_scales
         self.c = TableC(fmt, head_dim, scale_block if fmt == FMT_E4M3 else 0, 0, n_rows,
-                        _ptr(d_data), _ptr(d_scales))
+                        _table_ptr(d_data), _table_ptr(d_scales))
 
 
 def hash(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err=None, stream=None):

@@ -314,6 +314,20 @@ const char *engram_last_error(void) { return g_last_error.c_str(); }
 
 int32_t engram_abi_version(void) { return ENGRAM_ABI_VERSION; }
 
+int32_t engram_map_host(const void *host, const void **device)
+{
+    CHECK(host && device, ENGRAM_E_ARG, "engram map_host: NULL pointer");
+    void *d = nullptr;
+    const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void *>(host), 0);
+    if (e != hipSuccess)
+        (void)hipGetLastError();   // a refused pointer leaves no error for the next call
+    CHECK(e == hipSuccess && d, ENGRAM_E_ARG,
+          "engram map_host: %p is not pinned host memory the device can map (%s)", host,
+          hipGetErrorString(e));
+    *device = d;
+    return ENGRAM_OK;
+}
+
 int32_t engram_hash_batch(const engram_hash_tables *tables, const int32_t *d_ids, int64_t B,
                           int64_t T, int64_t start_pos, int64_t *d_history, int64_t max_seq,
                           int64_t *d_row_ids, int32_t *d_err, void *stream)

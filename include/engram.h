@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 2
+#define ENGRAM_ABI_VERSION 3
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -128,7 +128,9 @@ int32_t engram_hash_batch(const engram_hash_tables *tables, const int32_t *d_ids
 #define ENGRAM_FMT_Q2K 0
 #define ENGRAM_FMT_E4M3 1
 
-/* One layer's table, resident in device memory.
+/* One layer's table, in device memory or in pinned host memory mapped for
+ * the device (engram_map_host: the kernels then read the rows across the
+ * host link).
  *   ENGRAM_FMT_Q2K: d_data [n_rows][84] Q2_K blocks (16 bytes of 4-bit
  *       scale/min pairs, 64 bytes of 2-bit quants, fp16 d, fp16 dmin; GGML's
  *       k-quant block, which the pages name by size only), head_dim = 256,
@@ -147,6 +149,18 @@ typedef struct engram_table {
     const uint8_t *d_data;
     const float *d_scales;
 } engram_table;
+
+/* Tables larger than device memory can stay in host memory (atlascybernetics
+ * "engram_v41.rs": the pages read each step's 84-byte rows on the host, from
+ * checkpoint shards, with EngramRowReader).  Given a pointer into pinned host
+ * memory (hipHostMalloc, or a framework's pinned allocation), stores in
+ * *device the address under which the kernels read it; engram_table.d_data
+ * and d_scales may be such addresses.  A decode step reads only its cols rows
+ * a layer, so it pays the link's read latency (a few microseconds a launch);
+ * a long prefill's gather becomes bound by the link's rate for small reads.
+ *   ENGRAM_E_ARG for NULL pointers or memory the device cannot map (not
+ *   pinned); nothing is allocated or copied. */
+int32_t engram_map_host(const void *host, const void **device);
 
 /* rows[t*cols + c] = dequant(table row d_row_ids[t*id_stride + c]) as bf16
  * (atlascybernetics "engram_v41.rs", rows_from_q2k and layer_row_ids;

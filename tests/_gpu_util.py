@@ -48,7 +48,9 @@ def family_data(name):
 class Device:
     """The workload on the GPU: tables, wkv, qk, token map, hash tables."""
 
-    def __init__(self, name):
+    def __init__(self, name, host_tables=False):
+        """host_tables: keep the tables (and e4m3 scales) in pinned host
+        memory, read by the kernels across the host link."""
         import torch
         import gram_hashed_embedding_engram_amd as E
         self.w, self.ht, self.layers = family_data(name)
@@ -60,8 +62,10 @@ class Device:
         self.tab, self.wkv, self.wkvq, self.qk = [], [], [], []
         self._oracle_wkv = {}
         for L in self.layers:
-            data = torch.from_numpy(L["table"]).to(dev)
-            scales = None if L["scales"] is None else torch.from_numpy(L["scales"]).to(dev)
+            place = ((lambda a: torch.from_numpy(a).pin_memory()) if host_tables
+                     else (lambda a: torch.from_numpy(a).to(dev)))
+            data = place(L["table"])
+            scales = None if L["scales"] is None else place(L["scales"])
             self.tab.append(E.Table(data, scales, head_dim=w.head_dim, scale_block=w.scale_block))
             if L["wkv_q2k"] is None:
                 self.wkv.append(torch.from_numpy(L["wkv"].view(np.int16)).to(dev))

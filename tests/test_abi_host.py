@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 2
+    assert L.engram_abi_version() == 3
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
@@ -93,6 +93,15 @@ def test_hash_refusals(L):
     assert hb(3, T=10, start=8) == E.E_RANGE
     assert hb(3, ids=None) == E.E_ARG
     assert hb(0, ids=None) == E.OK and hb(3, T=0, ids=None) == E.OK
+
+
+def test_map_host_refusals(L):
+    # NULL host address or NULL result slot: refused before any runtime call
+    out = ctypes.c_void_p(0)
+    rc, msg = rc_msg(L.engram_map_host(None, ctypes.byref(out)))
+    assert rc == E.E_ARG and "NULL" in msg and out.value is None
+    buf = np.zeros(64, np.uint8)
+    assert L.engram_map_host(buf.ctypes.data, None) == E.E_ARG
 
 
 def test_gather_refusals(L):
