@@ -2,6 +2,7 @@
 // and dispatch to the kernels.  Every check runs before any launch, so a
 // refused call enqueues nothing (metrale "engram_v41" module index,
 // invariants: refusals happen before any copy or launch).
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,6 +33,28 @@ int32_t launch_status(const char *what)
     if (e != hipSuccess)
         return fail(ENGRAM_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return ENGRAM_OK;
+}
+
+constexpr int kMaxDevices = 64;
+
+int device_cus()
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 namespace {

@@ -205,6 +205,10 @@ int32_t launch_status(const char *what);
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Compute units of the current device, which sizes the grids of the
+// streaming kernels (queried once per device; 256 if the query fails).
+int device_cus();
+
 // Where a launcher enqueues: the stream, and optionally a pair of events the
 // runtime records with the dispatch of the launcher's first kernel and the
 // completion of its last (stage timing; null events = a plain launch).

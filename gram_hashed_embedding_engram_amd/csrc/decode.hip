@@ -546,14 +546,7 @@ int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const
                             uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows,
                             int32_t *err, int64_t B, const Launch &l)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
                        tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
                        row_ids, rows, err, hist_stride};
@@ -591,14 +584,7 @@ int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32
                       uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows, int32_t *err,
                       const Launch &l)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
                        tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
                        row_ids, rows, err, 0};

@@ -135,14 +135,7 @@ bool gemm_small_fits(int64_t M, int64_t K, int64_t N)
 int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
                           int64_t K, int64_t N, const Launch &l)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     // row tiles of 16 per workgroup: about one workgroup per CU (at most 6
     // tiles: beyond that the operand registers spill at four token tiles)
     const int64_t tiles = N / 16;

@@ -149,14 +149,7 @@ template <int NT>
 int32_t launch_multi(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, int64_t N,
                      const Launch &l)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     constexpr int NW = kGemvMultiThreads / 64;
     int64_t blocks = (N + NW - 1) / NW;
     if (blocks > cus)
@@ -186,14 +179,7 @@ template <int NT>
 int32_t launch_nt(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t K, int64_t N,
                   const Launch &l, bool first, bool last)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     const int64_t ni = (K + 511) / 512;
     int64_t blocks = (N + 3) / 4;
     const int64_t cap = (int64_t)cus * kGemvBlocksPerCu;

@@ -54,14 +54,7 @@ __global__ __launch_bounds__(kQ2kThreads, 8) void gemv_q2k_kernel(const uint16_t
 int32_t launch_gemv_q2k(const uint16_t *x, const uint8_t *w, uint16_t *y, int64_t K, int64_t N,
                         const Launch &l)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     int64_t blocks = (N + kQ2kThreads / 64 - 1) / (kQ2kThreads / 64);
     const int64_t cap = (int64_t)cus * kQ2kBlocksPerCu;
     if (blocks > cap)

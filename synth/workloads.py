@@ -116,9 +116,24 @@ ODD_Q2K = Workload(
 ODD_E4M3 = replace(ODD_Q2K, name="odd_cols_e4m3_2layer", family=6, fmt="e4m3")
 ODD_WKVQ2K = replace(ODD_Q2K, name="odd_cols_q2k_wkvq2k_2layer", wkv_fmt="q2k")
 
+# the largest hash geometries the library takes: 4 layers of 32 columns (128
+# hash slots, K 8192: the one-launch decode kernels' limit) with Q2_K tables,
+# and the longest n-gram (8) with 4 heads (28 columns a layer, 112 slots) with
+# e4m3 tables; small vocabularies and tables, hc * dim = 1024
+MAX_SLOTS_Q2K = Workload(
+    name="max_slots_q2k_4layer", family=7, vocab=1024, compressed=800, p_unmapped=0.10,
+    max_ngram=5, n_heads=8, n_layers=4, prime_lo=500, prime_hi=3000, fmt="q2k", dim=256,
+    hc=4, token_dist="uniform", prompt=8, decode_steps=16)
+MAX_NGRAM_E4M3 = Workload(
+    name="max_ngram_e4m3_4layer", family=8, vocab=1024, compressed=800, p_unmapped=0.10,
+    max_ngram=8, n_heads=4, n_layers=4, prime_lo=500, prime_hi=3000, fmt="e4m3", dim=256,
+    hc=4, token_dist="uniform", prompt=8, decode_steps=16)
+
 WORKLOADS = {w.name: w for w in (TINY_E4M3, DECODE_Q2K, PREFILL_Q2K, SPLIT_E4M3, GATHER_Q2K,
-                                 DECODE_WKVQ2K, ODD_Q2K, ODD_E4M3, ODD_WKVQ2K)}
+                                 DECODE_WKVQ2K, ODD_Q2K, ODD_E4M3, ODD_WKVQ2K, MAX_SLOTS_Q2K,
+                                 MAX_NGRAM_E4M3)}
 # seed index of each workload's token / highway stream (tables use `family`)
 STREAM_INDEX = {TINY_E4M3.name: 0, DECODE_Q2K.name: 1, PREFILL_Q2K.name: 2,
                 SPLIT_E4M3.name: 3, GATHER_Q2K.name: 4, DECODE_WKVQ2K.name: 5,
-                ODD_Q2K.name: 6, ODD_E4M3.name: 7, ODD_WKVQ2K.name: 8}
+                ODD_Q2K.name: 6, ODD_E4M3.name: 7, ODD_WKVQ2K.name: 8,
+                MAX_SLOTS_Q2K.name: 9, MAX_NGRAM_E4M3.name: 10}

@@ -119,12 +119,15 @@ def test_forward_decode_workload(E):
 
 
 @pytest.mark.parametrize("name", [synth.ODD_Q2K.name, synth.ODD_E4M3.name,
-                                  synth.ODD_WKVQ2K.name])
-def test_forward_odd_columns(E, name):
-    """An odd number of columns (5: K 1280, an odd number of 1 KiB loads a
-    row, a partial last sub-block round): 8-token prompt, then 24
-    single-token steps through the one-launch decode kernels, both layers,
-    every call against the oracle."""
+                                  synth.ODD_WKVQ2K.name, synth.MAX_SLOTS_Q2K.name,
+                                  synth.MAX_NGRAM_E4M3.name])
+def test_forward_edge_geometry(E, name):
+    """Edge-case hash geometries: an odd number of columns (5: K 1280, an
+    odd number of 1 KiB loads a row, a partial last sub-block round), the
+    most hash slots (4 layers x 32 columns = 128, K 8192) and the longest
+    n-gram (8, 4 layers x 28 columns).  A prompt, then single-token steps
+    through the one-launch decode kernels, every layer, every call against
+    the oracle."""
     dev = Device(name)
     w = dev.w
     log(f"forward: {name}, prompt {w.prompt} + {w.decode_steps} steps")
@@ -341,7 +344,8 @@ def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
 
 @pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name,
                                   synth.DECODE_WKVQ2K.name, synth.ODD_Q2K.name,
-                                  synth.ODD_E4M3.name, synth.ODD_WKVQ2K.name])
+                                  synth.ODD_E4M3.name, synth.ODD_WKVQ2K.name,
+                                  synth.MAX_SLOTS_Q2K.name, synth.MAX_NGRAM_E4M3.name])
 def test_fused_decode_matches_staged(E, name):
     """The one-launch decode layer (hash + gather + projection) leaves exactly
     what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""
@@ -451,7 +455,8 @@ def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
 
 @pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 2), (synth.DECODE_Q2K.name, 3),
                                     (synth.DECODE_Q2K.name, 4), (synth.ODD_Q2K.name, 3),
-                                    (synth.ODD_E4M3.name, 4)])
+                                    (synth.ODD_E4M3.name, 4), (synth.MAX_SLOTS_Q2K.name, 3),
+                                    (synth.MAX_NGRAM_E4M3.name, 2)])
 def test_fused_batched_decode_matches_staged(E, name, B):
     """B sequences' decode steps through the one-launch several-sequence
     kernel leave exactly what the staged kernels leave (row ids, rows, kv,
