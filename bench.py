@@ -457,6 +457,37 @@ def bench_split(args, torch, E, G, synth):
                     unit="engram tokens/s per layer"))
 
 
+def read_ceiling(torch, E, synth, reps=30):
+    """The device's practical read-stream rate: engram_stream_read over one
+    layer's wkv bytes at the decode shape, three buffers in turn (768 MB,
+    past the 256 MB last-level cache), so every launch reads HBM."""
+    w = synth.DECODE_Q2K
+    nbytes = w.N * w.K * 2
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda")
+            for i in range(3)]
+    sink = torch.zeros(E.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        E.stream_read(bufs[i], sink, stream)
+    torch.cuda.synchronize()
+    # the launches straight through the C ABI, so host overhead stays far
+    # below a launch's duration
+    fn, s_ptr, k_ptr = E.lib().engram_stream_read, stream.cuda_stream, sink.data_ptr()
+    ptrs = [b.data_ptr() for b in bufs]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(reps):
+        fn(ptrs[i % 3], nbytes, k_ptr, s_ptr)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / reps
+    del bufs
+    return dict(kernel="stream_read_kernel (12 KiB rows, 1 KiB non-temporal loads, "
+                       "no arithmetic)", bytes_per_launch=nbytes, avg_launch_us=us,
+                GBps=nbytes / (us / 1e6) / 1e9, frac_of_peak=nbytes / (us / 1e6) / 1e9 /
+                HBM_PEAK_GBPS)
+
+
 def cpu_baseline(res, synth, budget_s):
     """The oracle on the host cores over the first decode steps (both
     layers), until budget_s seconds of work have run."""
@@ -546,6 +577,8 @@ def main():
         print(json.dumps({"gather_stress": bench_gather_stress(args, torch, E, G, synth)}),
               flush=True)
         return
+    ceiling = read_ceiling(torch, E, synth)
+    log(f"read ceiling: {ceiling['avg_launch_us']:.2f} us a launch, {ceiling['GBps']:.0f} GB/s")
     inputs = device_inputs(synth.DECODE_Q2K, torch, E, G)
     dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=inputs)
     log(f"decode (fused): {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
@@ -614,7 +647,9 @@ def main():
                      "traffic": counter_traffic("decode_kernel_counters.md", "decode.hip"),
                      "kernel": "decode_kernel<Q2K,12> (hash + gather/dequant + projection of "
                                "one layer for one token; one launch per layer-step)",
-                     "bytes_per_launch": dec["proj_bytes"], "avg_launch_ms": dec["proj_avg_ms"]},
+                     "bytes_per_launch": dec["proj_bytes"], "avg_launch_ms": dec["proj_avg_ms"],
+                     "frac_of_read_ceiling": gbps / ceiling["GBps"]},
+        "hbm_read_ceiling": ceiling,
         "stages_ms_per_layer_step": dec["stages"],
         "decode_staged": {"ms_per_step": staged["ms_per_step"], "value": staged["value"],
                           "stages_ms_per_layer_step": staged["stages"],

@@ -18,6 +18,8 @@ E_ARG, E_RANGE, E_UNSUPPORTED, E_STATE, E_HIP, E_DEVICE = -1, -2, -3, -4, -5, -6
 DEVERR_TOKEN, DEVERR_ROW = 1, 2
 FMT_Q2K, FMT_E4M3 = 0, 1
 Q2K_ROW_BYTES = 84
+STREAM_ROW_BYTES = 12288      # engram_stream_read's row (ENGRAM_STREAM_ROW_BYTES)
+STREAM_SINK_WORDS = 8192      # its sink (ENGRAM_STREAM_SINK_WORDS)
 STAGES = ("hash", "gather", "project", "gate")
 
 # Every symbol include/engram.h declares.
@@ -30,7 +32,7 @@ EXPORTS = (
     "engram_forward",
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
-    "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host",
+    "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host", "engram_stream_read",
 )
 
 
@@ -99,6 +101,7 @@ def lib():
             "engram_ctx_timing": (i32, [p, p, p]),
             "engram_ctx_destroy": (None, [p]),
             "engram_map_host": (i32, [p, p]),
+            "engram_stream_read": (i32, [p, i64, p, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -223,6 +226,13 @@ def dequant_q2k(d_blocks, d_out, stream=None):
 def qk_product(d_q, d_k, d_qk, stream=None):
     _check(lib().engram_qk_product(_ptr(d_q), _ptr(d_k), _ptr(d_qk), int(d_q.numel()),
                                    _stream(stream)))
+
+
+def stream_read(d_src, d_sink, stream=None):
+    """Stream d_src once, one XOR fold per wavefront into d_sink [8192]
+    int32 (the read-rate yardstick; engram_stream_read)."""
+    _check(lib().engram_stream_read(_ptr(d_src), int(d_src.numel() * d_src.element_size()),
+                                    _ptr(d_sink), _stream(stream)))
 
 
 def gate_apply(d_h, d_kv, d_qk, eps, stream=None):

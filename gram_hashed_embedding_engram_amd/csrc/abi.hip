@@ -440,6 +440,18 @@ int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk,
     return launch_qk_product(d_q, d_k, d_qk, n, on(stream));
 }
 
+int32_t engram_stream_read(const void *d_src, int64_t bytes, uint32_t *d_sink, void *stream)
+{
+    CHECK(bytes > 0 && bytes % ENGRAM_STREAM_ROW_BYTES == 0, ENGRAM_E_ARG,
+          "engram stream_read: %lld bytes is not a positive multiple of %d", (long long)bytes,
+          ENGRAM_STREAM_ROW_BYTES);
+    CHECK(d_src && d_sink, ENGRAM_E_ARG, "engram stream_read: NULL pointer");
+    CHECK((reinterpret_cast<uintptr_t>(d_src) & 15) == 0 &&
+              (reinterpret_cast<uintptr_t>(d_sink) & 3) == 0,
+          ENGRAM_E_ARG, "engram stream_read: misaligned buffer");
+    return launch_stream_read(d_src, bytes, d_sink, on(stream));
+}
+
 int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, int64_t T,
                           int32_t hc, int64_t dim, float eps, void *stream)
 {

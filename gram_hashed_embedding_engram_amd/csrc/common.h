@@ -259,6 +259,7 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
                           const Launch &l);
 int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
+int32_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, const Launch &l);
 
 // One decode token through hash, gather + dequant and the projection of one
 // layer in a single launch (decode.hip).  first_layer: the token's compressed

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 3
+#define ENGRAM_ABI_VERSION 4
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -336,6 +336,22 @@ int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage /*[4]*/,
                           int64_t *launches_per_stage /*[4]*/);
 
 void engram_ctx_destroy(engram_ctx *ctx);
+
+/* ------------------------------------------------------------ measurement */
+
+/* Not a step of the method: the yardstick the streaming projections are
+ * measured against.  Reads d_src [bytes] once, in the decode projection's
+ * access pattern (each of 8192 wavefronts streams 12 KiB rows as 1 KiB
+ * non-temporal loads, the next row in flight while one is consumed),
+ * XOR-folds every 32-bit word and stores wavefront w's fold in d_sink[w]
+ * (d_sink [ENGRAM_STREAM_SINK_WORDS]): the XOR of the sink words is the XOR
+ * of every word of d_src.  Its rate over a buffer resident in HBM is the
+ * practical ceiling of a read stream on the device.
+ *   bytes: a positive multiple of ENGRAM_STREAM_ROW_BYTES; d_src 16-byte
+ *   aligned, d_sink 4-byte aligned (ENGRAM_E_ARG otherwise). */
+#define ENGRAM_STREAM_ROW_BYTES 12288
+#define ENGRAM_STREAM_SINK_WORDS 8192
+int32_t engram_stream_read(const void *d_src, int64_t bytes, uint32_t *d_sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 3
+    assert L.engram_abi_version() == 4
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
@@ -102,6 +102,19 @@ def test_map_host_refusals(L):
     assert rc == E.E_ARG and "NULL" in msg and out.value is None
     buf = np.zeros(64, np.uint8)
     assert L.engram_map_host(buf.ctypes.data, None) == E.E_ARG
+
+
+def test_stream_read_refusals(L):
+    R = E.STREAM_ROW_BYTES
+    assert "#define ENGRAM_STREAM_ROW_BYTES %d" % R in open(HEADER).read()
+    assert "#define ENGRAM_STREAM_SINK_WORDS %d" % E.STREAM_SINK_WORDS in open(HEADER).read()
+    rc, msg = rc_msg(L.engram_stream_read(FAKE, R + 4, FAKE, None))
+    assert rc == E.E_ARG and "multiple" in msg
+    assert L.engram_stream_read(FAKE, 0, FAKE, None) == E.E_ARG
+    assert L.engram_stream_read(None, R, FAKE, None) == E.E_ARG
+    assert L.engram_stream_read(FAKE, R, None, None) == E.E_ARG
+    rc, msg = rc_msg(L.engram_stream_read(FAKE + 8, R, FAKE, None))
+    assert rc == E.E_ARG and "misaligned" in msg
 
 
 def test_gather_refusals(L):

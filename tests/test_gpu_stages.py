@@ -469,3 +469,20 @@ def test_gate_rows_independent_of_T(E, dim):
         E.gate_apply(d_one, cuda(kv[t:t + 1].copy()), d_qk, 1e-6)
         np.testing.assert_array_equal(d_one.cpu().numpy().view(np.uint32),
                                       d_all[t:t + 1].cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", [1, 37, 20480])
+def test_stream_read_folds_every_word(E, rows):
+    """The read-rate yardstick reads every word of its buffer exactly once:
+    the XOR of its sink words equals the XOR of all the buffer's 32-bit
+    words (1 row: most wavefronts have no row; 20480 rows: one layer's wkv
+    bytes at the decode shape)."""
+    rng = np.random.default_rng(rows)
+    words = rows * E.STREAM_ROW_BYTES // 4
+    src = rng.integers(0, 2**32, size=words, dtype=np.uint64).astype(np.uint32)
+    want = np.bitwise_xor.reduce(src)
+    d_src = torch.from_numpy(src.view(np.int32)).cuda()
+    sink = torch.full((E.STREAM_SINK_WORDS,), -1, dtype=torch.int32, device="cuda")
+    E.stream_read(d_src, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want, f"{got:#x} != {want:#x}"
