@@ -102,13 +102,17 @@ __device__ __forceinline__ SlotConsts slot_consts(const HashConsts &c)
 // Hash of the token and gather + dequant of this layer's cols rows into the
 // activations s_x by the NT threads of a workgroup (every workgroup;
 // workgroup 0 also writes the row ids, the history entry and the dequantised
-// rows).  Ends with s_x complete, chunk c at slot xslot(c).  The token, its look-back and (Q2_K) the
-// table blocks come through the scalar cache, so nothing here waits for the
-// weight loads the kernel has in flight.
-template <int FMT, int NT>
+// rows).  Ends with s_x complete, chunk c at slot xslot(c).  The token, its
+// look-back and (Q2_K) the table blocks come through the scalar cache, so
+// nothing here waits for the weight loads the kernel issued before the call.
+// e4m3 rows (256 bytes and their scales) are too large to stage through
+// scalar registers: their vector loads go out first and the kernel's first
+// weight row right after them (issue_row, called here for e4m3 tables only),
+// so waiting for the table leaves the row in flight.
+template <int FMT, int NT, class IssueRow>
 __device__ __forceinline__ void decode_prologue(const HashConsts &c, const DecodeArgs &a,
                                                 const SlotConsts &sc, int64_t *s_id,
-                                                uint32_t *s_blk, u32x4 *s_x)
+                                                uint32_t *s_blk, u32x4 *s_x, IssueRow &&issue_row)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, and known so
@@ -216,17 +220,31 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
             s_x[xslot(ch)] = s_id[r] >= 0 ? q2k_dequant8(s_blk + r * 21, ch & 31) : zero;
         }
     } else {
+        // this thread's chunks tid, tid + NT, ...: every load unconditional
+        // (past kc: the last chunk again; a missing row: row 0), all issued
+        // before the weight row
+        constexpr int NCH = kMaxChunks / NT;
         const int nb = 256 / a.scale_block;
-        for (int ch = tid; ch < kc; ch += NT) {
-            const int r = ch >> 5, sub = ch & 31;
+        uint32_t w0[NCH], w1[NCH];
+        float sv[NCH];
+        bool live[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; j++) {
+            const int ch = min(tid + j * NT, (int)kc - 1), r = ch >> 5, sub = ch & 31;
             const int64_t id = s_id[r];
-            u32x4 o = zero;
-            if (id >= 0) {
-                const uint32_t *b = (const uint32_t *)(a.table + id * 256 + 8 * sub);
-                o = e4m3_dequant8(b[0], b[1], a.scales[id * nb + (8 * sub) / a.scale_block]);
-            }
-            s_x[xslot(ch)] = o;
+            live[j] = tid + j * NT < kc && id >= 0;
+            const int64_t idc = id >= 0 ? id : 0;
+            const uint32_t *b = (const uint32_t *)(a.table + idc * 256 + 8 * sub);
+            w0[j] = b[0];
+            w1[j] = b[1];
+            sv[j] = a.scales[idc * nb + (8 * sub) / a.scale_block];
         }
+        __builtin_amdgcn_sched_barrier(0);      // the table loads stay ahead of the row's
+        issue_row();
+#pragma unroll
+        for (int j = 0; j < NCH; j++)
+            if (tid + j * NT < kc)
+                s_x[xslot(tid + j * NT)] = live[j] ? e4m3_dequant8(w0[j], w1[j], sv[j]) : zero;
     }
     __syncthreads();
     if (blockIdx.x == 0)
@@ -251,17 +269,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const HashConsts c, const D
 
     // ---- this thread's hash constants, then the first wkv row of this
     // wavefront (past the row's end, lanes load its last chunk again: loads
-    // are unconditional, and the staged order never reads those chunks)
+    // are unconditional, and the staged order never reads those chunks) --
+    // with an e4m3 table, inside the prologue right after the table loads
     const SlotConsts sc = slot_consts(c);
     u32x4 wv[NI];
-    {
+    auto issue_row = [&] {
         const u32x4 *wr = (const u32x4 *)(w + min(wave, N - 1) * K);
 #pragma unroll
         for (int i = 0; i < NI; i++)
             wv[i] = __builtin_nontemporal_load(wr + min((int64_t)i * 64 + lane, kc - 1));
-    }
+    };
+    if constexpr (FMT == ENGRAM_FMT_Q2K)
+        issue_row();
 
-    decode_prologue<FMT, 256>(c, a, sc, s_id, s_blk, s_x);
+    decode_prologue<FMT, 256>(c, a, sc, s_id, s_blk, s_x, issue_row);
 
     // ---- projection: rows wave, wave + n_waves, ...  A row's result is
     // stored after the next row's loads are issued, so the loop's wait for
@@ -316,12 +337,17 @@ __global__ __launch_bounds__(kQ2kwThreads, 8) void decode_q2kw_kernel(const Hash
     const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const uint32_t *wd = (const uint32_t *)wq;
 
-    // ---- this thread's hash constants, then the first row's blocks
+    // ---- this thread's hash constants, then the first row's blocks (with
+    // an e4m3 table: inside the prologue, after the table loads)
     const SlotConsts sc = slot_consts(c);
     uint32_t r[NLD];
-    q2k_row_load<NLD>(wd + min(wave, N - 1) * row_dwords, row_dwords, lane, r);
+    auto issue_row = [&] {
+        q2k_row_load<NLD>(wd + min(wave, N - 1) * row_dwords, row_dwords, lane, r);
+    };
+    if constexpr (FMT == ENGRAM_FMT_Q2K)
+        issue_row();
 
-    decode_prologue<FMT, kQ2kwThreads>(c, a, sc, s_id, s_blk, s_x);
+    decode_prologue<FMT, kQ2kwThreads>(c, a, sc, s_id, s_blk, s_x, issue_row);
 
     // ---- projection, one row per wavefront at a time
     for (int64_t n = wave; n < N; n += n_waves) {

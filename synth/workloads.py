@@ -115,6 +115,7 @@ ODD_Q2K = Workload(
     hc=4, token_dist="uniform", prompt=8, decode_steps=24)
 ODD_E4M3 = replace(ODD_Q2K, name="odd_cols_e4m3_2layer", family=6, fmt="e4m3")
 ODD_WKVQ2K = replace(ODD_Q2K, name="odd_cols_q2k_wkvq2k_2layer", wkv_fmt="q2k")
+ODD_E4M3_WKVQ2K = replace(ODD_E4M3, name="odd_cols_e4m3_wkvq2k_2layer", wkv_fmt="q2k")
 
 # the largest hash geometries the library takes: 4 layers of 32 columns (128
 # hash slots, K 8192: the one-launch decode kernels' limit) with Q2_K tables,
@@ -130,10 +131,10 @@ MAX_NGRAM_E4M3 = Workload(
     hc=4, token_dist="uniform", prompt=8, decode_steps=16)
 
 WORKLOADS = {w.name: w for w in (TINY_E4M3, DECODE_Q2K, PREFILL_Q2K, SPLIT_E4M3, GATHER_Q2K,
-                                 DECODE_WKVQ2K, ODD_Q2K, ODD_E4M3, ODD_WKVQ2K, MAX_SLOTS_Q2K,
-                                 MAX_NGRAM_E4M3)}
+                                 DECODE_WKVQ2K, ODD_Q2K, ODD_E4M3, ODD_WKVQ2K, ODD_E4M3_WKVQ2K,
+                                 MAX_SLOTS_Q2K, MAX_NGRAM_E4M3)}
 # seed index of each workload's token / highway stream (tables use `family`)
 STREAM_INDEX = {TINY_E4M3.name: 0, DECODE_Q2K.name: 1, PREFILL_Q2K.name: 2,
                 SPLIT_E4M3.name: 3, GATHER_Q2K.name: 4, DECODE_WKVQ2K.name: 5,
                 ODD_Q2K.name: 6, ODD_E4M3.name: 7, ODD_WKVQ2K.name: 8,
-                MAX_SLOTS_Q2K.name: 9, MAX_NGRAM_E4M3.name: 10}
+                MAX_SLOTS_Q2K.name: 9, MAX_NGRAM_E4M3.name: 10, ODD_E4M3_WKVQ2K.name: 11}

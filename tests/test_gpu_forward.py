@@ -119,8 +119,8 @@ def test_forward_decode_workload(E):
 
 
 @pytest.mark.parametrize("name", [synth.ODD_Q2K.name, synth.ODD_E4M3.name,
-                                  synth.ODD_WKVQ2K.name, synth.MAX_SLOTS_Q2K.name,
-                                  synth.MAX_NGRAM_E4M3.name])
+                                  synth.ODD_WKVQ2K.name, synth.ODD_E4M3_WKVQ2K.name,
+                                  synth.MAX_SLOTS_Q2K.name, synth.MAX_NGRAM_E4M3.name])
 def test_forward_edge_geometry(E, name):
     """Edge-case hash geometries: an odd number of columns (5: K 1280, an
     odd number of 1 KiB loads a row, a partial last sub-block round), the
@@ -345,7 +345,8 @@ def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
 @pytest.mark.parametrize("name", [synth.DECODE_Q2K.name, synth.TINY_E4M3.name,
                                   synth.DECODE_WKVQ2K.name, synth.ODD_Q2K.name,
                                   synth.ODD_E4M3.name, synth.ODD_WKVQ2K.name,
-                                  synth.MAX_SLOTS_Q2K.name, synth.MAX_NGRAM_E4M3.name])
+                                  synth.ODD_E4M3_WKVQ2K.name, synth.MAX_SLOTS_Q2K.name,
+                                  synth.MAX_NGRAM_E4M3.name])
 def test_fused_decode_matches_staged(E, name):
     """The one-launch decode layer (hash + gather + projection) leaves exactly
     what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""
@@ -424,7 +425,8 @@ def test_map_host_refuses_unpinned_memory(E):
     assert ei.value.code == E.E_ARG
 
 
-@pytest.mark.parametrize("name", [synth.DECODE_WKVQ2K.name, synth.ODD_WKVQ2K.name])
+@pytest.mark.parametrize("name", [synth.DECODE_WKVQ2K.name, synth.ODD_WKVQ2K.name,
+                                  synth.ODD_E4M3_WKVQ2K.name])
 def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
     """Workloads with Q2_K wkv: every step through the kernels over the
     blocks (one launch or staged) leaves exactly what the bf16 kernels over
