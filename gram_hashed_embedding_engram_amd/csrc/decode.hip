@@ -392,14 +392,25 @@ __global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
     const int64_t pos = a.pos;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // ---- the first wkv row of this wavefront (past the row's end: its last
-    // chunk again)
+    // ---- this lane's hash slot constants (slot = lane: layer slot / cols,
+    // column slot % cols), then the first wkv row of this wavefront (past
+    // the row's end: its last chunk again).  The constants are taken right
+    // after the row's loads are issued, in every wavefront: their loads stay
+    // ahead of the row's, and the wait for them leaves the row in flight.
     const int slot = min(lane, nslots - 1);
+    const int sl = slot / cols;
+    int64_t m[ENGRAM_MAX_NGRAM];
+#pragma unroll
+    for (int k = 0; k < ENGRAM_MAX_NGRAM; k++)      // in bounds: l*ng + k < MAX_LAYERS*MAX_NGRAM
+        m[k] = c.mult[sl * c.ng + k];
+    const int64_t prime = c.prime[slot], offset = c.offset[slot];
     const u32x4 *wr0 = (const u32x4 *)(w + min(wave, N - 1) * K);
     u32x4 wv[NI];
 #pragma unroll
     for (int i = 0; i < NI; i++)
         wv[i] = __builtin_nontemporal_load(wr0 + min(i * 64 + lane, kc - 1));
+    asm volatile("" ::"v"(prime), "v"(offset), "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]),
+                 "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]));
 
     // ---- hash of sequence b = wid
     if (wid < NB) {
@@ -424,32 +435,7 @@ __global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
                 win[k] = q >= 0 ? v : -1;
             }
         }
-        const int l = slot / cols, col = slot - l * cols;
-        // slot i's prime and offset into lane i: scalar loads of the kernel
-        // arguments moved into lanes (v_writelane), no vector loads
-        uint32_t p_lo = 1u, p_hi = 0u, o_lo = 0u, o_hi = 0u;
-#pragma unroll
-        for (int i = 0; i < 64; i++) {
-            if (i < nslots) {
-                const uint64_t pi = (uint64_t)c.prime[i], oi = (uint64_t)c.offset[i];
-                asm("v_writelane_b32 %0, %1, %2" : "+v"(p_lo) : "s"((uint32_t)pi), "i"(i));
-                asm("v_writelane_b32 %0, %1, %2" : "+v"(p_hi) : "s"((uint32_t)(pi >> 32)), "i"(i));
-                asm("v_writelane_b32 %0, %1, %2" : "+v"(o_lo) : "s"((uint32_t)oi), "i"(i));
-                asm("v_writelane_b32 %0, %1, %2" : "+v"(o_hi) : "s"((uint32_t)(oi >> 32)), "i"(i));
-            }
-        }
-        const int64_t prime = (int64_t)(((uint64_t)p_hi << 32) | p_lo);
-        const int64_t offset = (int64_t)(((uint64_t)o_hi << 32) | o_lo);
-        int64_t m[ENGRAM_MAX_NGRAM];
-#pragma unroll
-        for (int k = 0; k < ENGRAM_MAX_NGRAM; k++)
-            m[k] = 0;
-        for (int ll = 0; ll < c.nl; ll++)
-#pragma unroll
-            for (int k = 0; k < ENGRAM_MAX_NGRAM; k++) {
-                const int64_t mk = k < c.ng ? c.mult[ll * c.ng + k] : 0;
-                m[k] = l == ll ? mk : m[k];
-            }
+        const int l = sl, col = slot - l * cols;
         if (lane < nslots && (l == a.layer || (blockIdx.x == 0 && a.first_layer))) {
             const int ngram = col / c.nh + 2;     // column (n-2)*n_heads + head
             bool blocked = win[0] == -1;
