@@ -223,7 +223,7 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
         // this thread's chunks tid, tid + NT, ...: every load unconditional
         // (past kc: the last chunk again; a missing row: row 0), all issued
         // before the weight row
-        constexpr int NCH = kMaxChunks / NT;
+        constexpr int NCH = (kMaxChunks + NT - 1) / NT;
         const int nb = 256 / a.scale_block;
         uint32_t w0[NCH], w1[NCH];
         float sv[NCH];
