@@ -200,8 +200,10 @@ def bench_decode(args, torch, E, G, synth, fused=True, inputs=None, w=None):
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
+    host_ms = (time.perf_counter() - t0) * 1e3
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -217,6 +219,7 @@ def bench_decode(args, torch, E, G, synth, fused=True, inputs=None, w=None):
     res = dict(
         fused=fused,
         ms_per_step=ms / args.steps,
+        host_ms_per_step=host_ms / args.steps,
         value=args.steps * nl / (ms / 1e3),
         proj_avg_ms=proj_ms / proj_n,
         proj_bytes=(decode_q2kw_bytes(w) if w.wkv_fmt == "q2k" else decode_bytes(w)) if fused
@@ -229,6 +232,71 @@ def bench_decode(args, torch, E, G, synth, fused=True, inputs=None, w=None):
         res["gather_GBps"] = w.cols * (84 + 512 + 8) / (g_ms / g_n / 1e3) / 1e9
     del ctx
     return res
+
+
+def bench_decode_graph(args, torch, E, G, synth, inputs):
+    """The decode workload's steps replayed from a hipGraph: after the prompt,
+    graph mode moves the position to the device and one step (both layers'
+    one-launch decode kernel and gate) is captured once; each timed step
+    writes the next token id into the captured id buffer (a device copy) and
+    replays the graph.  The highway buffer is the captured one, gated in place
+    step after step."""
+    w = synth.DECODE_Q2K
+    ht, tm, tables, layers, host = inputs
+    n_tok = w.prompt + 2 * args.warmup + args.steps + 1
+    ids = G.token_ids(w, n_tok)
+    d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    prompt_h = torch.from_numpy(G.highway(w, w.prompt)).cuda()
+    h = torch.from_numpy(G.highway(w, 1, decode=True)).cuda()
+    ctx = make_ctx(E, w, tables, layers, w.prompt, n_tok)
+    for l in range(w.n_layers):
+        ctx.forward(l, d_ids[:w.prompt], w.prompt, prompt_h)
+    ctx.set_graph_mode(True)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(w.n_layers):
+            ctx.forward(l, tok if l == 0 else None, 1, h)
+    stream = torch.cuda.current_stream()
+    pos = w.prompt
+
+    def step(copy):
+        nonlocal pos
+        if copy:
+            tok.copy_(d_ids[pos:pos + 1])
+        g.replay()
+        pos += 1
+
+    def timed(copy, n):
+        for _ in range(args.warmup):
+            step(copy)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step(copy)
+        host = (time.perf_counter() - t0) * 1e3 / n
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n, host
+
+    half = args.steps // 2
+    ms_copy, host_copy = timed(True, half)
+    ms_replay, host_replay = timed(False, args.steps - half)
+    ctx.check()
+    ctx.set_graph_mode(False)
+    assert ctx.position == pos, (ctx.position, pos)
+    del g, ctx
+    return dict(ms_per_step=ms_copy, value=w.n_layers / (ms_copy / 1e3),
+                host_ms_per_step=host_copy, replay_only_ms_per_step=ms_replay,
+                replay_only_host_ms_per_step=host_replay,
+                unit="engram tokens/s per layer",
+                how="one captured step (both layers) replayed per token, after a device copy "
+                    "of the token id into the captured buffer (replay_only: the same buffer "
+                    "content replayed, no copy)")
 
 
 def bench_decode_batched(args, torch, E, G, synth, inputs, B):
@@ -592,6 +660,11 @@ def main():
         log(f"decode (host tables): {host_dec['ms_per_step'] * 1e3:.1f} us/step, "
             f"stages(ms) {host_dec['stages']}")
         del hinputs
+    graph = bench_decode_graph(args, torch, E, G, synth, inputs)
+    log(f"decode (graph replay): {graph['ms_per_step'] * 1e3:.1f} us/step with the token copy, "
+        f"{graph['replay_only_ms_per_step'] * 1e3:.1f} us/step replay only; host "
+        f"{graph['host_ms_per_step'] * 1e3:.1f} / {graph['replay_only_host_ms_per_step'] * 1e3:.1f}"
+        f" us/step (eager {dec['host_ms_per_step'] * 1e3:.1f})")
     batched = []
     for B in args.batch_sequences:
         r = bench_decode_batched(args, torch, E, G, synth, inputs, B)
@@ -651,6 +724,7 @@ def main():
                      "frac_of_read_ceiling": gbps / ceiling["GBps"]},
         "hbm_read_ceiling": ceiling,
         "stages_ms_per_layer_step": dec["stages"],
+        "host_ms_per_step": dec["host_ms_per_step"],
         "decode_staged": {"ms_per_step": staged["ms_per_step"], "value": staged["value"],
                           "stages_ms_per_layer_step": staged["stages"],
                           "gemv_GBps": staged_gbps, "gather_GBps": staged["gather_GBps"],
@@ -668,6 +742,7 @@ def main():
             "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
             "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
                        "stages_ms_per_layer_step": decq_staged["stages"]}},
+        "decode_graph": graph,
         "decode_host_tables": None if host_dec is None else {
             "tables": "pinned host memory, rows read across the host link",
             "ms_per_step": host_dec["ms_per_step"], "value": host_dec["value"],

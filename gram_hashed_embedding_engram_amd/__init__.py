@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libengram.so")
 
 OK = 0
 E_ARG, E_RANGE, E_UNSUPPORTED, E_STATE, E_HIP, E_DEVICE = -1, -2, -3, -4, -5, -6
-DEVERR_TOKEN, DEVERR_ROW = 1, 2
+DEVERR_TOKEN, DEVERR_ROW, DEVERR_POSITION = 1, 2, 4
 FMT_Q2K, FMT_E4M3 = 0, 1
 Q2K_ROW_BYTES = 84
 STREAM_ROW_BYTES = 12288      # engram_stream_read's row (ENGRAM_STREAM_ROW_BYTES)
@@ -33,6 +33,7 @@ EXPORTS = (
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
     "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host", "engram_stream_read",
+    "engram_ctx_set_graph_mode",
 )
 
 
@@ -102,6 +103,7 @@ def lib():
             "engram_ctx_destroy": (None, [p]),
             "engram_map_host": (i32, [p, p]),
             "engram_stream_read": (i32, [p, i64, p, p]),
+            "engram_ctx_set_graph_mode": (i32, [p, i32, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -320,6 +322,11 @@ class Context:
 
     def set_timing(self, on: bool):
         _check(lib().engram_ctx_set_timing(self.h, 1 if on else 0))
+
+    def set_graph_mode(self, on: bool, stream=None):
+        """Single-token steps read their position from the device, so their
+        launches can be captured once and replayed (engram_ctx_set_graph_mode)."""
+        _check(lib().engram_ctx_set_graph_mode(self.h, 1 if on else 0, _stream(stream)))
 
     def timing(self):
         ms = (ctypes.c_double * 4)()

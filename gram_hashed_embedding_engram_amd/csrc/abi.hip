@@ -251,6 +251,10 @@ struct engram_ctx {
     bool fused_decode = true;
     bool was_reset = false;
     bool timing = false;
+    // graph mode: one-token decode steps read their position from *d_pos
+    // (in the workspace's error slot), which the step's last gate advances
+    bool graph_mode = false;
+    int64_t *d_pos = nullptr;
     std::vector<TimingRec> recs;
     std::vector<hipEvent_t> pool;
 };
@@ -287,6 +291,16 @@ bool carve(const engram_config *cfg, Carve *c)
     off += 256;
     c->total = off;
     return true;
+}
+
+// The step that layer 0 just hashed (at ctx->step_start, T tokens a
+// sequence) is open for the other layers; the position moves past it.
+void open_step(engram_ctx *ctx, int64_t T)
+{
+    if (!ctx->graph_mode)       // (graph mode: the position moves on the device)
+        ctx->pos = ctx->step_start + T;
+    ctx->step_open = true;
+    ctx->step_T = T;
 }
 
 hipEvent_t take_event(engram_ctx *ctx)
@@ -514,6 +528,7 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
     ctx->rows = (uint16_t *)(ws + cv.rows);
     ctx->kv = (uint16_t *)(ws + cv.kv);
     ctx->err = (int32_t *)(ws + cv.err);
+    ctx->d_pos = (int64_t *)(ws + cv.err + 8);
     *out = ctx;
     return ENGRAM_OK;
 }
@@ -598,7 +613,8 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     CHECK(d_h && aligned(d_h, 16), ENGRAM_E_ARG, "engram forward: highway NULL or misaligned");
     if (hash_index == 0) {
         CHECK(d_ids, ENGRAM_E_ARG, "engram forward: NULL token ids");
-        CHECK(ctx->pos + T <= ctx->cfg.max_seq, ENGRAM_E_RANGE,
+        // (graph mode: the position lives on the device, which checks it)
+        CHECK(ctx->graph_mode || ctx->pos + T <= ctx->cfg.max_seq, ENGRAM_E_RANGE,
               "engram hasher: %lld positions, %lld needed", (long long)ctx->cfg.max_seq,
               (long long)(ctx->pos + T));
     } else {
@@ -613,60 +629,67 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     const engram_config &cfg = ctx->cfg;
     const int64_t B = batch_of(&cfg), M = B * T;   // tokens of the call, sequence-major
     int32_t rc;
+    const bool one_launch = M == 1 && ctx->fused_decode && cfg.head_dim == 256 &&
+                            ctx->cols <= kDecodeMaxCols;
+    const bool one_launch_multi = T == 1 && B >= 2 && B <= kDecodeMultiMaxB &&
+                                  ctx->fused_decode && !L.wkv_q2k && cfg.head_dim == 256 &&
+                                  ctx->cols <= kDecodeMaxCols && ctx->nl * ctx->cols <= 64;
+    CHECK(!ctx->graph_mode || one_launch || one_launch_multi, ENGRAM_E_STATE,
+          "engram forward: graph mode runs single-token steps through the one-launch decode "
+          "kernels only (T = %lld, %lld sequences)", (long long)T, (long long)B);
+    // layer 0 opens a new step at the current position; the step (and the
+    // position's advance) takes effect once the launch that hashes it is
+    // enqueued, so a refused launch leaves no half-open step behind
+    if (hash_index == 0) {
+        ctx->step_open = false;
+        ctx->step_start = ctx->pos;
+    }
+    // graph mode: the kernels read the step's position from the device word,
+    // and the last layer's gate moves it on
+    const DecodePos dpos{ctx->step_start, ctx->graph_mode ? ctx->d_pos : nullptr, cfg.max_seq};
+    int64_t *advance = ctx->graph_mode && hash_index == ctx->nl - 1 ? ctx->d_pos : nullptr;
     // one decode token of one sequence: hash, gather and projection in one launch
-    if (M == 1 && ctx->fused_decode && cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols) {
-        if (hash_index == 0) {
-            ctx->step_start = ctx->pos;
-            ctx->pos += 1;
-            ctx->step_open = true;
-            ctx->step_T = 1;
-        }
+    if (one_launch) {
         rc = staged(ctx, 2, s, [&](const Launch &l) {
-            return launch_decode(ctx->consts, cfg.hash.d_token_map, d_ids, ctx->step_start,
-                                 ctx->history, hash_index, hash_index == 0, L.tab, L.wkv,
-                                 L.wkv_q2k, ctx->kv,
+            return launch_decode(ctx->consts, cfg.hash.d_token_map, d_ids, dpos, ctx->history,
+                                 hash_index, hash_index == 0, L.tab, L.wkv, L.wkv_q2k, ctx->kv,
                                  ctx->kv_width, ctx->row_ids, ctx->rows, ctx->err, l);
         });
         if (rc != ENGRAM_OK)
             return rc;
+        if (hash_index == 0)
+            open_step(ctx, 1);
         return staged(ctx, 3, s, [&](const Launch &l) {
-            return launch_gate(d_h, ctx->kv, L.qk, 1, cfg.hc, cfg.dim, cfg.eps, l);
+            return launch_gate(d_h, ctx->kv, L.qk, 1, cfg.hc, cfg.dim, cfg.eps, l, advance,
+                               cfg.max_seq);
         });
     }
     // one decode token of each of 2..4 sequences: the same, all tokens in one
     // pass over the weights
-    if (T == 1 && B >= 2 && B <= kDecodeMultiMaxB && ctx->fused_decode && !L.wkv_q2k &&
-        cfg.head_dim == 256 && ctx->cols <= kDecodeMaxCols && ctx->nl * ctx->cols <= 64) {
-        if (hash_index == 0) {
-            ctx->step_start = ctx->pos;
-            ctx->pos += 1;
-            ctx->step_open = true;
-            ctx->step_T = 1;
-        }
+    if (one_launch_multi) {
         rc = staged(ctx, 2, s, [&](const Launch &l) {
-            return launch_decode_multi(ctx->consts, cfg.hash.d_token_map, d_ids, ctx->step_start,
+            return launch_decode_multi(ctx->consts, cfg.hash.d_token_map, d_ids, dpos,
                                        ctx->history, cfg.max_seq, hash_index, hash_index == 0,
                                        L.tab, L.wkv, ctx->kv, ctx->kv_width, ctx->row_ids,
                                        ctx->rows, ctx->err, B, l);
         });
         if (rc != ENGRAM_OK)
             return rc;
+        if (hash_index == 0)
+            open_step(ctx, 1);
         return staged(ctx, 3, s, [&](const Launch &l) {
-            return launch_gate(d_h, ctx->kv, L.qk, M, cfg.hc, cfg.dim, cfg.eps, l);
+            return launch_gate(d_h, ctx->kv, L.qk, M, cfg.hc, cfg.dim, cfg.eps, l, advance,
+                               cfg.max_seq);
         });
     }
     if (hash_index == 0) {
-        const int64_t start = ctx->pos;
         rc = staged(ctx, 0, s, [&](const Launch &l) {
-            return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, B, T, start,
+            return launch_hash(ctx->consts, cfg.hash.d_token_map, d_ids, B, T, ctx->step_start,
                                ctx->history, cfg.max_seq, ctx->row_ids, ctx->err, l);
         });
         if (rc != ENGRAM_OK)
             return rc;
-        ctx->step_start = ctx->pos;
-        ctx->pos += T;
-        ctx->step_open = true;
-        ctx->step_T = T;
+        open_step(ctx, T);
     }
     const int64_t K = (int64_t)ctx->cols * cfg.head_dim;
     rc = staged(ctx, 1, s, [&](const Launch &l) {
@@ -695,9 +718,10 @@ int32_t engram_check(engram_ctx *ctx, void *stream)
     int32_t word = 0;
     e = hipMemcpy(&word, ctx->err, sizeof word, hipMemcpyDeviceToHost);
     CHECK(e == hipSuccess, ENGRAM_E_HIP, "engram check: %s", hipGetErrorString(e));
-    CHECK(word == 0, ENGRAM_E_DEVICE, "engram device error 0x%x:%s%s", word,
+    CHECK(word == 0, ENGRAM_E_DEVICE, "engram device error 0x%x:%s%s%s", word,
           (word & ENGRAM_DEVERR_TOKEN) ? " token id outside the vocabulary" : "",
-          (word & ENGRAM_DEVERR_ROW) ? " row id outside the table" : "");
+          (word & ENGRAM_DEVERR_ROW) ? " row id outside the table" : "",
+          (word & ENGRAM_DEVERR_POSITION) ? " a replayed step past max_seq" : "");
     return ENGRAM_OK;
 }
 
@@ -721,6 +745,8 @@ int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t 
 int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable)
 {
     CHECK(ctx, ENGRAM_E_ARG, "engram fused decode: NULL context");
+    CHECK(enable || !ctx->graph_mode, ENGRAM_E_STATE,
+          "engram fused decode: graph mode needs the one-launch kernels");
     ctx->fused_decode = enable != 0;
     return ENGRAM_OK;
 }
@@ -728,7 +754,36 @@ int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable)
 int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable)
 {
     CHECK(ctx, ENGRAM_E_ARG, "engram timing: NULL context");
+    CHECK(!(enable && ctx->graph_mode), ENGRAM_E_STATE,
+          "engram timing: not in graph mode (its events cannot be captured)");
     ctx->timing = enable != 0;
+    return ENGRAM_OK;
+}
+
+int32_t engram_ctx_set_graph_mode(engram_ctx *ctx, int32_t enable, void *stream)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram graph mode: NULL context");
+    CHECK(ctx->was_reset, ENGRAM_E_STATE, "engram graph mode: the context needs engram_reset first");
+    if (enable) {
+        CHECK(!ctx->timing, ENGRAM_E_STATE, "engram graph mode: stage timing is on");
+        CHECK(ctx->fused_decode, ENGRAM_E_STATE, "engram graph mode: one-launch decode is off");
+        if (!ctx->graph_mode) {
+            const int32_t rc = launch_set_word(ctx->d_pos, ctx->pos, on(stream));
+            if (rc != ENGRAM_OK)
+                return rc;
+        }
+        ctx->graph_mode = true;
+        return ENGRAM_OK;
+    }
+    if (ctx->graph_mode) {
+        hipError_t e = hipStreamSynchronize(as_stream(stream));
+        CHECK(e == hipSuccess, ENGRAM_E_HIP, "engram graph mode: %s", hipGetErrorString(e));
+        int64_t p = 0;
+        e = hipMemcpy(&p, ctx->d_pos, sizeof p, hipMemcpyDeviceToHost);
+        CHECK(e == hipSuccess, ENGRAM_E_HIP, "engram graph mode: %s", hipGetErrorString(e));
+        ctx->pos = p;
+        ctx->graph_mode = false;
+    }
     return ENGRAM_OK;
 }
 

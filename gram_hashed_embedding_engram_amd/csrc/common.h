@@ -222,8 +222,11 @@ template <class F, class... Args>
 inline void dispatch(F kernel, dim3 grid, dim3 block, const Launch &l, bool first, bool last,
                      Args... args)
 {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, l.stream, first ? l.start : nullptr,
-                          last ? l.stop : nullptr, 0, args...);
+    hipEvent_t start = first ? l.start : nullptr, stop = last ? l.stop : nullptr;
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, l.stream, start, stop, 0, args...);
+    else   // a plain launch, which stream capture records as a kernel node
+        hipLaunchKernelGGL(kernel, grid, block, 0, l.stream, args...);
 }
 
 // Hash constants, passed by value as a kernel argument.
@@ -254,8 +257,12 @@ int32_t launch_dequant_q2k(const uint8_t *blocks, int64_t n_blocks, uint16_t *ou
                            const Launch &l);
 int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t K,
                     int64_t N, const Launch &l);
+// advance (nullable): a device position word that workgroup 0 moves one
+// step on, up to max_seq, after its row (the last layer of a replayed step)
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
-                    int64_t dim, float eps, const Launch &l);
+                    int64_t dim, float eps, const Launch &l, int64_t *advance = nullptr,
+                    int64_t max_seq = 0);
+int32_t launch_set_word(int64_t *p, int64_t v, const Launch &l);
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
                           const Launch &l);
 int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l);
@@ -271,13 +278,20 @@ int32_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, const
 // The one-launch decode step of B = 2..kDecodeMultiMaxB sequences at one
 // position (history [B][hist_stride]); bf16 wkv; n_layers*cols <= 64.
 constexpr int64_t kDecodeMultiMaxB = 4;
+// The position of a decode step: the host's value, or (word non-null: graph
+// replay) a device word holding it, checked on the device against max_seq.
+struct DecodePos {
+    int64_t pos;
+    const int64_t *word;
+    int64_t max_seq;
+};
 int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
-                            int64_t pos, int64_t *history, int64_t hist_stride, int32_t layer,
+                            const DecodePos &pos, int64_t *history, int64_t hist_stride, int32_t layer,
                             bool first_layer, const engram_table &tab, const uint16_t *w,
                             uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows,
                             int32_t *err, int64_t B, const Launch &l);
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
-                      int64_t pos, int64_t *history, int32_t layer, bool first_layer,
+                      const DecodePos &pos, int64_t *history, int32_t layer, bool first_layer,
                       const engram_table &tab, const uint16_t *w, const uint8_t *w_q2k,
                       uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows, int32_t *err,
                       const Launch &l);

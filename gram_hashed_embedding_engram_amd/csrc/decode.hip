@@ -57,6 +57,8 @@ struct DecodeArgs {
     uint16_t *rows;
     int32_t *err;
     int64_t hist_stride;     // history entries per sequence (several sequences)
+    const int64_t *pos_word; // non-null: the step's position is read here (graph replay)
+    int64_t max_seq;         // history entries a sequence, for that position's check
 };
 
 // A load of a value that no thread writes during the launch, through the
@@ -75,6 +77,21 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The step's position: the kernel argument, or -- for a replayed graph --
+// the device word the previous step's last gate advanced.  A position past
+// the history is reported (ok = false) and clamped, so reads stay in bounds
+// and nothing is written there.
+__device__ __forceinline__ int64_t step_pos(const DecodeArgs &a, bool &ok)
+{
+    if (!a.pos_word) {
+        ok = true;
+        return a.pos;
+    }
+    const int64_t p = cload(a.pos_word);
+    ok = p >= 0 && p < a.max_seq;
+    return ok ? p : (p < 0 ? 0 : a.max_seq - 1);
 }
 
 // The hash constants of the slot thread tid computes (layer tid / cols,
@@ -118,7 +135,8 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, and known so
     const int cols = c.cols;
     const int64_t kc = (int64_t)cols * 32;
-    const int64_t pos = a.pos;
+    bool pos_ok;
+    const int64_t pos = step_pos(a, pos_ok);
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
     // ---- the token's compressed id and its look-back (win[k]: k positions
@@ -163,9 +181,12 @@ __device__ __forceinline__ void decode_prologue(const HashConsts &c, const Decod
             if (blockIdx.x == 0) {
                 a.row_ids[slot] = id;
                 if (tid == 0 && a.first_layer) {
-                    a.history[pos] = win[0];
+                    if (pos_ok)
+                        a.history[pos] = win[0];
                     if (bad && a.err)
                         atomicOr(a.err, ENGRAM_DEVERR_TOKEN);
+                    if (!pos_ok && a.err)
+                        atomicOr(a.err, ENGRAM_DEVERR_POSITION);
                 }
             }
             if (l == a.layer) {
@@ -389,7 +410,8 @@ __global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
     const int kc = cols * 32, kcp = (kc + 127) & ~127, n_sb = cols * 16;
     const int64_t wave = (int64_t)blockIdx.x * NW + wid;
     const int64_t n_waves = (int64_t)gridDim.x * NW;
-    const int64_t pos = a.pos;
+    bool pos_ok;
+    const int64_t pos = step_pos(a, pos_ok);
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
     // ---- this lane's hash slot constants (slot = lane: layer slot / cols,
@@ -451,9 +473,12 @@ __global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
             if (blockIdx.x == 0) {
                 a.row_ids[(int64_t)b * nslots + slot] = id;
                 if (lane == 0 && a.first_layer) {
-                    hist[pos] = win[0];
+                    if (pos_ok)
+                        hist[pos] = win[0];
                     if (bad && a.err)
                         atomicOr(a.err, ENGRAM_DEVERR_TOKEN);
+                    if (!pos_ok && a.err)
+                        atomicOr(a.err, ENGRAM_DEVERR_POSITION);
                 }
             }
             if (l == a.layer) {
@@ -553,15 +578,15 @@ __global__ __launch_bounds__(kDecodeMultiThreads) void decode_multi_kernel(
 }  // namespace
 
 int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
-                            int64_t pos, int64_t *history, int64_t hist_stride, int32_t layer,
+                            const DecodePos &pos, int64_t *history, int64_t hist_stride, int32_t layer,
                             bool first_layer, const engram_table &tab, const uint16_t *w,
                             uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows,
                             int32_t *err, int64_t B, const Launch &l)
 {
     const int cus = device_cus();
-    const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
+    const DecodeArgs a{token_map, ids,    pos.pos,  history, layer, first_layer ? 1 : 0,
                        tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
-                       row_ids, rows, err, hist_stride};
+                       row_ids, rows, err, hist_stride, pos.word, pos.max_seq};
     const int ni = (c.cols * 256 + 511) / 512;
     int64_t blocks = (N + 15) / 16;
     if (blocks > cus)
@@ -591,15 +616,15 @@ int32_t launch_decode_multi(const HashConsts &c, const int64_t *token_map, const
 }
 
 int32_t launch_decode(const HashConsts &c, const int64_t *token_map, const int32_t *ids,
-                      int64_t pos, int64_t *history, int32_t layer, bool first_layer,
+                      const DecodePos &pos, int64_t *history, int32_t layer, bool first_layer,
                       const engram_table &tab, const uint16_t *w, const uint8_t *w_q2k,
                       uint16_t *y, int64_t N, int64_t *row_ids, uint16_t *rows, int32_t *err,
                       const Launch &l)
 {
     const int cus = device_cus();
-    const DecodeArgs a{token_map, ids,    pos,  history, layer, first_layer ? 1 : 0,
+    const DecodeArgs a{token_map, ids,    pos.pos,  history, layer, first_layer ? 1 : 0,
                        tab.d_data, tab.d_scales, tab.n_rows, tab.scale_block, 0, y, N,
-                       row_ids, rows, err, 0};
+                       row_ids, rows, err, 0, pos.word, pos.max_seq};
     const int64_t K = (int64_t)c.cols * 256;
     int64_t blocks = (N + 3) / 4;
     const int64_t cap = (int64_t)cus * kDecodeBlocksPerCu;

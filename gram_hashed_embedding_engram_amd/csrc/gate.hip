@@ -175,12 +175,25 @@ __device__ __forceinline__ int64_t token_row(int64_t b, int64_t T, int hc)
     return ((k << 3) + (b & 7)) * hc + c;
 }
 
+// The step's position word, moved on by one (up to max_seq) once workgroup
+// 0's row is done: the last layer of a replayed decode step.  No other
+// thread of the launch reads it.
+__device__ __forceinline__ void advance_step(int64_t *advance, int64_t max_seq)
+{
+    if (advance && blockIdx.x == 0 && threadIdx.x == 0) {
+        const int64_t v = *advance;
+        if (v < max_seq)
+            *advance = v + 1;
+    }
+}
+
 template <int MAXI>
 __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
                                                    const uint16_t *__restrict__ kv,
                                                    const float *__restrict__ qk, int64_t T,
                                                    int hc, int64_t dim, float eps, float fdim,
-                                                   float inv_sqrt_dim)
+                                                   float inv_sqrt_dim, int64_t *advance,
+                                                   int64_t max_seq)
 {
     const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
@@ -188,6 +201,7 @@ __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
     const uint16_t *kvt = kv + t * (hc + 1) * dim;
     gate_row<MAXI>(h + row * dim, kvt + (int64_t)c * dim, qk + (int64_t)c * dim,
                    kvt + (int64_t)hc * dim, (int)(dim >> 8), eps, fdim, inv_sqrt_dim);
+    advance_step(advance, max_seq);
 }
 
 // Any multiple of 256 (h is read again for the update).
@@ -195,7 +209,8 @@ __global__ __launch_bounds__(256) void gate_kernel_any(float *__restrict__ h,
                                                        const uint16_t *__restrict__ kv,
                                                        const float *__restrict__ qk, int64_t T,
                                                        int hc, int64_t dim, float eps,
-                                                       float fdim, float inv_sqrt_dim)
+                                                       float fdim, float inv_sqrt_dim,
+                                                       int64_t *advance, int64_t max_seq)
 {
     const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
@@ -203,6 +218,7 @@ __global__ __launch_bounds__(256) void gate_kernel_any(float *__restrict__ h,
     const uint16_t *kvt = kv + t * (hc + 1) * dim;
     gate_row_any(h + row * dim, kvt + (int64_t)c * dim, qk + (int64_t)c * dim,
                  kvt + (int64_t)hc * dim, (int)(dim >> 8), eps, fdim, inv_sqrt_dim);
+    advance_step(advance, max_seq);
 }
 
 __global__ __launch_bounds__(256) void qk_kernel(const uint16_t *__restrict__ q,
@@ -212,6 +228,12 @@ __global__ __launch_bounds__(256) void qk_kernel(const uint16_t *__restrict__ q,
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         qk[i] = __uint_as_float((uint32_t)q[i] << 16) * __uint_as_float((uint32_t)k[i] << 16);
+}
+
+__global__ __launch_bounds__(64) void set_word_kernel(int64_t *__restrict__ p, int64_t v)
+{
+    if (threadIdx.x == 0)
+        *p = v;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p, int64_t words)
@@ -224,7 +246,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 }  // namespace
 
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
-                    int64_t dim, float eps, const Launch &l)
+                    int64_t dim, float eps, const Launch &l, int64_t *advance, int64_t max_seq)
 {
     const int64_t rows = T * hc;
     if (rows == 0)
@@ -236,14 +258,14 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
 #define ENGRAM_GATE_CASE(I_)                                                                   \
     case I_:                                                                                   \
         dispatch(gate_kernel<I_>, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps, \
-                 fdim, inv_sqrt_dim);                                                         \
+                 fdim, inv_sqrt_dim, advance, max_seq);                                       \
         break;
     switch (maxi) {
         ENGRAM_GATE_CASE(1) ENGRAM_GATE_CASE(2) ENGRAM_GATE_CASE(3) ENGRAM_GATE_CASE(4)
         ENGRAM_GATE_CASE(5) ENGRAM_GATE_CASE(6) ENGRAM_GATE_CASE(7) ENGRAM_GATE_CASE(8)
     default:
         dispatch(gate_kernel_any, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps,
-                 fdim, inv_sqrt_dim);
+                 fdim, inv_sqrt_dim, advance, max_seq);
         break;
     }
 #undef ENGRAM_GATE_CASE
@@ -261,6 +283,12 @@ int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64
         blocks = 4096;
     dispatch(qk_kernel, dim3((unsigned)blocks), dim3(256), l, true, true, q, k, qk, n);
     return launch_status("engram qk kernel");
+}
+
+int32_t launch_set_word(int64_t *p, int64_t v, const Launch &l)
+{
+    dispatch(set_word_kernel, dim3(1), dim3(64), l, true, true, p, v);
+    return launch_status("engram set-word kernel");
 }
 
 int32_t launch_fill_zero(void *p, size_t bytes, const Launch &l)

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 4
+#define ENGRAM_ABI_VERSION 5
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -53,6 +53,7 @@ extern "C" {
 /* bits of the device error word */
 #define ENGRAM_DEVERR_TOKEN 1      /* token id < 0 or >= vocab                     */
 #define ENGRAM_DEVERR_ROW 2        /* row id < 0 or >= the table's row count       */
+#define ENGRAM_DEVERR_POSITION 4   /* graph mode: a step past max_seq              */
 
 /* limits of the hash geometry (the hash constants travel as kernel arguments) */
 #define ENGRAM_MAX_LAYERS 4
@@ -334,6 +335,29 @@ int32_t engram_ctx_set_fused_decode(engram_ctx *ctx, int32_t enable);
 int32_t engram_ctx_set_timing(engram_ctx *ctx, int32_t enable);
 int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage /*[4]*/,
                           int64_t *launches_per_stage /*[4]*/);
+
+/* Graph mode, for replaying captured decode steps (atlascybernetics
+ * "spark_model/layers/deepseek_v41_layer.rs", GraphMode and the per-layer
+ * graphs: a decode step's launches are captured once with fixed pointers and
+ * replayed, and an oracle mode compares replay with eager execution bit for
+ * bit).  While enabled, each
+ * engram_forward must be a single-token step of the one-launch decode kernels
+ * (T = 1 and the conditions of engram_ctx_set_fused_decode, or 2-4 sequences
+ * with at most 64 hash slots; anything else: ENGRAM_E_STATE), and its kernels
+ * read the step's position from a device word in the workspace instead of
+ * taking it from the host: the gate of the last hash index moves the word on
+ * by one, so the same launches, captured into a hipGraph on `stream`, replay
+ * successive steps.  The caller writes each step's token ids into the d_ids
+ * buffer it captured (and its highway into d_h) before a replay.  The host
+ * no longer checks the position: a step at max_seq or beyond sets
+ * ENGRAM_DEVERR_POSITION, writes no history and leaves its outputs
+ * unspecified.  Stage timing must be off (its events cannot be captured).
+ *   enable = 1: enqueues the store of the host's position into the device
+ *   word on `stream` (nothing if already enabled).  enable = 0: synchronises
+ *   `stream` and reads the device word back as the host's position
+ *   (engram_position).  ENGRAM_E_STATE before the first engram_reset, with
+ *   timing on, or with the one-launch decode kernels off. */
+int32_t engram_ctx_set_graph_mode(engram_ctx *ctx, int32_t enable, void *stream);
 
 void engram_ctx_destroy(engram_ctx *ctx);
 

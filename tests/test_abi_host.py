@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 4
+    assert L.engram_abi_version() == 5
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
@@ -262,6 +262,10 @@ def test_context_refusals_and_state(L):
         # a valid call before the first engram_reset (nothing is launched)
         rc, msg = rc_msg(L.engram_forward(h, 0, FAKE, 1, FAKE, None))
         assert rc == E.E_STATE and "engram_reset" in msg
+        # graph mode likewise needs the reset (the device position starts there)
+        rc, msg = rc_msg(L.engram_ctx_set_graph_mode(h, 1, None))
+        assert rc == E.E_STATE and "engram_reset" in msg
+        assert L.engram_ctx_set_graph_mode(None, 1, None) == E.E_ARG
         # timing with nothing recorded makes no runtime call
         assert L.engram_ctx_set_timing(h, 1) == E.OK
         ms = (ctypes.c_double * 4)()

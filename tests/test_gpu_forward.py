@@ -415,6 +415,92 @@ def test_host_tables_match_device_tables(E, name, B):
                 np.testing.assert_array_equal(x, y, err_msg=f"call {i}: {what}")
 
 
+def decode_steps_eager(dev, B, ids, hp, hs, prompt, steps):
+    """Reference: the prompt, then single-token steps through the one-launch
+    kernels, eagerly; per step the row ids, the last layer's rows and kv, and
+    every layer's highway (each layer gated from the step's fresh highway)."""
+    w = dev.w
+    ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps, batch=B)
+    d_ids = cuda(ids.astype(np.int32))
+    for layer in range(w.n_layers):
+        ctx.forward(layer, d_ids[:, :prompt].contiguous() if layer == 0 else None, prompt,
+                    torch.from_numpy(np.ascontiguousarray(hp)).cuda())
+    out = []
+    for step in range(steps):
+        hl = []
+        for layer in range(w.n_layers):
+            d_h = torch.from_numpy(np.ascontiguousarray(hs[step][:, None])).cuda()
+            ctx.forward(layer, d_ids[:, prompt + step:prompt + step + 1].contiguous()
+                        if layer == 0 else None, 1, d_h)
+            hl.append(d_h.cpu().numpy().view(np.uint32))
+        rid, rows, kv = ctx.views(1)
+        out.append((rid.cpu().numpy(), to_np_u16(rows), to_np_u16(kv), hl))
+    ctx.check()
+    return out
+
+
+@pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 1), (synth.ODD_E4M3.name, 1),
+                                    (synth.DECODE_WKVQ2K.name, 1), (synth.DECODE_Q2K.name, 3)])
+def test_graph_replay_matches_eager(E, name, B):
+    """A decode step captured once into a hipGraph in graph mode (the kernels
+    read the step's position from the device; the last layer's gate advances
+    it) and replayed step after step, with the token and highway buffers
+    refilled eagerly between replays, leaves exactly what eager steps leave:
+    row ids, rows, kv and every layer's highway, bit for bit (the pages' graph
+    oracle mode).  A replay past max_seq is reported, and the device position
+    comes back to the host when graph mode ends."""
+    dev = Device(name)
+    w = dev.w
+    prompt, steps = 8, 12
+    log(f"graph replay vs eager: {name}, B={B}")
+    ids = G.token_ids(w, B * (prompt + steps)).reshape(B, prompt + steps)
+    hp = G.highway(w, B * prompt).reshape(B, prompt, w.hc, w.dim)
+    hs = G.highway(w, B * steps).reshape(steps, B, w.hc, w.dim)
+    want = decode_steps_eager(dev, B, ids, hp, hs, prompt, steps)
+
+    ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps, batch=B)
+    d_ids = cuda(ids.astype(np.int32))
+    for layer in range(w.n_layers):
+        ctx.forward(layer, d_ids[:, :prompt].contiguous() if layer == 0 else None, prompt,
+                    torch.from_numpy(np.ascontiguousarray(hp)).cuda())
+    ctx.set_graph_mode(True)
+    with pytest.raises(E.EngramError) as ei:          # many tokens: not in graph mode
+        ctx.forward(0, d_ids[:, :2].contiguous(), 2, torch.zeros(B, 2, w.hc, w.dim).cuda())
+    assert ei.value.code == E.E_STATE
+    tok = torch.zeros(B, 1, dtype=torch.int32, device="cuda")
+    hbuf = [torch.zeros(B, 1, w.hc, w.dim, dtype=torch.float32, device="cuda")
+            for _ in range(w.n_layers)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for layer in range(w.n_layers):
+            ctx.forward(layer, tok if layer == 0 else None, 1, hbuf[layer])
+    for step in range(steps):
+        tok.copy_(d_ids[:, prompt + step:prompt + step + 1])
+        h0 = torch.from_numpy(np.ascontiguousarray(hs[step][:, None])).cuda()
+        for hb in hbuf:
+            hb.copy_(h0)
+        g.replay()
+        torch.cuda.synchronize()
+        rid, rows, kv = ctx.views(1)
+        wr, wrows, wkv, wh = want[step]
+        np.testing.assert_array_equal(rid.cpu().numpy(), wr, err_msg=f"step {step} row ids")
+        np.testing.assert_array_equal(to_np_u16(rows), wrows, err_msg=f"step {step} rows")
+        np.testing.assert_array_equal(to_np_u16(kv), wkv, err_msg=f"step {step} kv")
+        for layer in range(w.n_layers):
+            np.testing.assert_array_equal(hbuf[layer].cpu().numpy().view(np.uint32), wh[layer],
+                                          err_msg=f"step {step} layer {layer} highway")
+    ctx.check()
+    # one replay past max_seq: reported on the device, position held at max_seq
+    g.replay()
+    with pytest.raises(E.EngramError) as ei:
+        ctx.check()
+    assert ei.value.code == E.E_DEVICE and "max_seq" in str(ei.value)
+    ctx.set_graph_mode(False)
+    assert ctx.position == prompt + steps
+    del g
+
+
 def test_map_host_refuses_unpinned_memory(E):
     """Only pinned host memory is mapped for the device; pageable memory is
     refused with E_ARG before any kernel could read it."""
