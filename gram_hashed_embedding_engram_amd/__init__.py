@@ -33,7 +33,7 @@ EXPORTS = (
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
     "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host", "engram_stream_read",
-    "engram_ctx_set_graph_mode",
+    "engram_ctx_set_graph_mode", "engram_ctx_set_position",
 )
 
 
@@ -104,6 +104,7 @@ def lib():
             "engram_map_host": (i32, [p, p]),
             "engram_stream_read": (i32, [p, i64, p, p]),
             "engram_ctx_set_graph_mode": (i32, [p, i32, p]),
+            "engram_ctx_set_position": (i32, [p, i64, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -322,6 +323,18 @@ class Context:
 
     def set_timing(self, on: bool):
         _check(lib().engram_ctx_set_timing(self.h, 1 if on else 0))
+
+    def history(self):
+        """The hasher's history rows, a view of the workspace: [batch, max_seq]
+        int64 compressed ids (what a checkpoint of the sequence holds)."""
+        import torch
+        n = self.batch * int(self.cfg.max_seq)
+        return self.workspace[:8 * n].view(torch.int64).view(self.batch, -1)
+
+    def set_position(self, pos, stream=None):
+        """Resume at pos over history rows the caller restored into the
+        workspace (engram_ctx_set_position)."""
+        _check(lib().engram_ctx_set_position(self.h, int(pos), _stream(stream)))
 
     def set_graph_mode(self, on: bool, stream=None):
         """Single-token steps read their position from the device, so their

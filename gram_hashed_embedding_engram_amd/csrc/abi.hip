@@ -727,6 +727,25 @@ int32_t engram_check(engram_ctx *ctx, void *stream)
 
 int64_t engram_position(const engram_ctx *ctx) { return ctx ? ctx->pos : -1; }
 
+int32_t engram_ctx_set_position(engram_ctx *ctx, int64_t pos, void *stream)
+{
+    CHECK(ctx, ENGRAM_E_ARG, "engram set position: NULL context");
+    CHECK(pos >= 0 && pos <= ctx->cfg.max_seq, ENGRAM_E_RANGE,
+          "engram set position: %lld outside 0..%lld", (long long)pos,
+          (long long)ctx->cfg.max_seq);
+    const Launch l = on(stream);
+    int32_t rc = launch_fill_zero(ctx->err, 256, l);     // error word (and device position)
+    if (rc == ENGRAM_OK && ctx->graph_mode)
+        rc = launch_set_word(ctx->d_pos, pos, l);
+    if (rc != ENGRAM_OK)
+        return rc;
+    ctx->pos = pos;
+    ctx->step_open = false;
+    ctx->step_T = 0;
+    ctx->was_reset = true;
+    return ENGRAM_OK;
+}
+
 int32_t engram_ctx_buffers(const engram_ctx *ctx, int64_t **d_row_ids, uint16_t **d_rows,
                            uint16_t **d_kv, int32_t **d_err)
 {

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 5
+#define ENGRAM_ABI_VERSION 6
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -288,6 +288,16 @@ int32_t engram_ctx_set_wkv_q2k(engram_ctx *ctx, int32_t hash_index, const uint8_
 
 /* History := 0, position := 0, device error word := 0, no step open. */
 int32_t engram_reset(engram_ctx *ctx, void *stream);
+
+/* Resume a sequence: the history rows in the workspace (engram_ctx_buffers'
+ * layout: [batch][max_seq] int64 at the workspace's start) hold the
+ * compressed ids of the first pos tokens, restored by the caller (say from a
+ * checkpoint of an earlier context's workspace); the next step hashes at pos.
+ * The hasher's state is exactly those entries and the position, so the steps
+ * that follow equal an uninterrupted run's.  No step is open afterwards; the
+ * device error word is cleared (on `stream`); in graph mode the device
+ * position is set too.  pos in 0..max_seq (ENGRAM_E_RANGE otherwise). */
+int32_t engram_ctx_set_position(engram_ctx *ctx, int64_t pos, void *stream);
 
 /* One engram layer over the next T tokens of every sequence, gating d_h
  * [batch][T][hc][dim] in place.  hash_index 0 opens a step: it hashes the

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 5
+    assert L.engram_abi_version() == 6
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
@@ -266,6 +266,12 @@ def test_context_refusals_and_state(L):
         rc, msg = rc_msg(L.engram_ctx_set_graph_mode(h, 1, None))
         assert rc == E.E_STATE and "engram_reset" in msg
         assert L.engram_ctx_set_graph_mode(None, 1, None) == E.E_ARG
+        # resuming: the position must lie in 0..max_seq (checked before any launch)
+        rc, msg = rc_msg(L.engram_ctx_set_position(h, 513, None))
+        assert rc == E.E_RANGE and "outside 0..512" in msg
+        assert L.engram_ctx_set_position(h, -1, None) == E.E_RANGE
+        assert L.engram_ctx_set_position(None, 0, None) == E.E_ARG
+        assert L.engram_position(h) == 0
         # timing with nothing recorded makes no runtime call
         assert L.engram_ctx_set_timing(h, 1) == E.OK
         ms = (ctypes.c_double * 4)()

@@ -501,6 +501,58 @@ def test_graph_replay_matches_eager(E, name, B):
     del g
 
 
+@pytest.mark.parametrize("name,B,fused", [(synth.DECODE_Q2K.name, 1, True),
+                                          (synth.ODD_E4M3.name, 2, True),
+                                          (synth.TINY_E4M3.name, 1, False)])
+def test_resume_from_restored_history(E, name, B, fused):
+    """A sequence resumed in a fresh context -- its history rows copied in
+    from the first context's workspace, the position set -- continues exactly
+    as the uninterrupted context: row ids, rows, kv and highway, bit for bit."""
+    dev = Device(name)
+    w = dev.w
+    prompt, before, after = 8, 5, 7
+    total = prompt + before + after
+    log(f"resume: {name}, B={B}, fused={fused}")
+    ids = G.token_ids(w, B * total).reshape(B, total)
+    hp = G.highway(w, B * prompt).reshape(B, prompt, w.hc, w.dim)
+    hs = G.highway(w, B * (before + after)).reshape(before + after, B, w.hc, w.dim)
+    d_ids = cuda(ids.astype(np.int32))
+
+    def step(ctx, p, h0):
+        T = h0.shape[1]
+        out = []
+        for layer in range(w.n_layers):
+            d_h = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
+            ctx.forward(layer, d_ids[:, p:p + T].contiguous() if layer == 0 else None, T, d_h)
+            rid, rows, kv = ctx.views(T)
+            out.append((rid.cpu().numpy(), to_np_u16(rows), to_np_u16(kv),
+                        d_h.cpu().numpy().view(np.uint32)))
+        return out
+
+    a = dev.context(max_tokens=prompt, max_seq=total, batch=B)
+    a.set_fused_decode(fused)
+    step(a, 0, hp)
+    for k in range(before):
+        step(a, prompt + k, hs[k][:, None])
+    pos = prompt + before
+    assert a.position == pos
+    saved = a.history().clone()
+    b = dev.context(max_tokens=prompt, max_seq=total, batch=B)
+    b.set_fused_decode(fused)
+    b.history().copy_(saved)
+    b.set_position(pos)
+    assert b.position == pos
+    for k in range(before, before + after):
+        got = step(b, prompt + k, hs[k][:, None])
+        want = step(a, prompt + k, hs[k][:, None])
+        for i, (x, y) in enumerate(zip(got, want)):
+            for u, v, what in zip(x, y, ("row ids", "rows", "kv", "highway")):
+                np.testing.assert_array_equal(u, v, err_msg=f"step {k} layer {i}: {what}")
+    a.check()
+    b.check()
+    torch.testing.assert_close(b.history(), a.history(), rtol=0, atol=0)
+
+
 def test_map_host_refuses_unpinned_memory(E):
     """Only pinned host memory is mapped for the device; pageable memory is
     refused with E_ARG before any kernel could read it."""
