@@ -73,8 +73,9 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
-                               "(the engram path has no non-HIP fallback)")
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m "
+                               "gram_hashed_embedding_engram_amd.build (the engram path has no "
+                               "non-HIP fallback)")
         L = ctypes.CDLL(LIB_PATH)
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         sig = {

@@ -20,7 +20,7 @@
  * Built with -ffp-contract=off so every f32 product and sum is rounded on its
  * own, as the pages' Rust evaluates them.
  *
- * Readings taken where the pages are silent (listed again in the design doc):
+ * Readings taken where the pages are silent:
  *   - Q2_K block layout: the pages give only its size (84 bytes, one block per
  *     256-wide row).  The layout used is GGML's k-quant block: 16 scale bytes
  *     (low nibble = sub-block scale, high nibble = sub-block min), 64 bytes of
