@@ -1,0 +1,54 @@
+"""The benchmark's host-side bookkeeping, without a GPU: the algorithmic byte
+counts its rooflines divide by, the source digest that decides whether a
+committed counter summary still describes the kernels, and the one-GPU
+guard."""
+import os
+import subprocess
+import sys
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_decode_bytes_per_launch():
+    # wkv 20480 x 6144 bf16 + 24 blocks of 84 B + kv 20480 bf16 + rows 6144 bf16
+    # + both layers' 48 row ids + token id, map entry and 4 history entries
+    w = synth.DECODE_Q2K
+    want = 20480 * 6144 * 2 + 24 * 84 + 20480 * 2 + 6144 * 2 + 2 * 24 * 8 + 4 + 8 + 8 * 4
+    assert bench.decode_bytes(w) == want == 251_713_932
+    # wkv as Q2_K blocks: 20480 rows of 24 blocks of 84 B instead of the bf16 matrix
+    wq = synth.DECODE_WKVQ2K
+    assert bench.decode_q2kw_bytes(wq) == want - 20480 * 6144 * 2 + 20480 * 24 * 84 == 41_343_372
+
+
+def test_source_digest_ignores_comments_only(tmp_path, monkeypatch):
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    (csrc / "k.hip").write_text('#include "h.h"\nint f() { return 1; }  // one\n')
+    (csrc / "h.h").write_text("int g();\n")
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    d0 = bench.source_digest("k.hip")
+    (csrc / "k.hip").write_text('#include "h.h"\n// a new comment\n\nint f() { return 1; }\n')
+    assert bench.source_digest("k.hip") == d0
+    (csrc / "h.h").write_text("int g(int);\n")          # an included header's code counts
+    assert bench.source_digest("k.hip") != d0
+
+
+def test_counter_traffic_needs_the_current_digest(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    digest = bench.source_digest("decode.hip")
+    (tmp_path / "cur.md").write_text(
+        f"source_sha256_16: {digest}\nhbm_bytes_per_launch: 252040986\n")
+    (tmp_path / "old.md").write_text(
+        "source_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 252040986\n")
+    assert bench.counter_traffic("cur.md", "decode.hip") == 252040986.0
+    assert bench.counter_traffic("old.md", "decode.hip") is None
+    assert bench.counter_traffic("missing.md", "decode.hip") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "single MI355X" in r.stderr
