@@ -92,3 +92,22 @@ def test_token_streams():
     assert counts[0] > 0.05 * z.size
     u = G.token_ids(synth.GATHER_Q2K)
     assert u.shape == (16384,) and np.bincount(u).max() < 10
+
+
+def test_workload_registry():
+    """Every workload has its own token / highway stream; workloads that share
+    a table family share its hash geometry, vocabulary and table format (they
+    reuse the same seeded tables); distinct primes fit each prime range."""
+    import synth
+    from synth import generate as G
+    names = list(synth.WORKLOADS)
+    from synth.workloads import STREAM_INDEX
+    assert sorted(STREAM_INDEX) == sorted(names)
+    assert len(set(STREAM_INDEX.values())) == len(names)
+    fam = {}
+    for w in synth.WORKLOADS.values():
+        key = (w.vocab, w.compressed, w.p_unmapped, w.max_ngram, w.n_heads, w.n_layers,
+               w.prime_lo, w.prime_hi, w.fmt, w.head_dim, w.scale_block)
+        assert fam.setdefault(w.family, key) == key, w.name
+        n_primes = len(G.primes_in(w.prime_lo, w.prime_hi))
+        assert n_primes >= w.n_layers * w.cols, w.name
