@@ -356,7 +356,7 @@ def bench_prefill(args, torch, E, G, synth):
     ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
     T = w.prompt
     reps = args.prefill_steps
-    warm = 2
+    warm = 3
     ids = G.token_ids(w)
     d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
     h = torch.from_numpy(G.highway(w, T)).cuda()
@@ -370,13 +370,16 @@ def bench_prefill(args, torch, E, G, synth):
     for _ in range(warm):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps):
+    # an event between consecutive steps (one record per ~2 ms step) for the
+    # per-step median beside the whole region's mean
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
         step()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    ms = ev[0].elapsed_time(ev[reps])
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
     ctx.set_timing(True)
     for _ in range(reps):
         step()
@@ -390,8 +393,9 @@ def bench_prefill(args, torch, E, G, synth):
     tflops = flops / (gemm_ms / 1e3) / 1e12
     gate_bytes = T * w.hc * w.dim * 8 + T * w.N * 2
     return dict(
-        workload=w.name, T=T, layers=w.n_layers,
+        workload=w.name, T=T, layers=w.n_layers, steps=reps, warmup=warm,
         ms_per_step=ms / reps,
+        median_ms_per_step=per_step[reps // 2],
         value=reps * T * w.n_layers / (ms / 1e3),
         unit="engram tokens/s per layer",
         stages_ms={k: v[0] / max(1, v[1]) for k, v in stages.items()},
@@ -592,7 +596,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the many-token legs (prefill, gather stress, e4m3 split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
