@@ -467,6 +467,10 @@ def test_graph_replay_matches_eager(E, name, B):
     with pytest.raises(E.EngramError) as ei:          # many tokens: not in graph mode
         ctx.forward(0, d_ids[:, :2].contiguous(), 2, torch.zeros(B, 2, w.hc, w.dim).cuda())
     assert ei.value.code == E.E_STATE
+    for refused in (lambda: ctx.set_timing(True), lambda: ctx.set_fused_decode(False)):
+        with pytest.raises(E.EngramError) as ei:      # nothing a capture could not replay
+            refused()
+        assert ei.value.code == E.E_STATE
     tok = torch.zeros(B, 1, dtype=torch.int32, device="cuda")
     hbuf = [torch.zeros(B, 1, w.hc, w.dim, dtype=torch.float32, device="cuda")
             for _ in range(w.n_layers)]
