@@ -407,6 +407,39 @@ def bench_prefill(args, torch, E, G, synth):
     )
 
 
+def bench_tiny(args, torch, E, G, synth, reps=50):
+    """The small e4m3 workload (one layer, T 64, K 1024, N 1280): whole
+    forwards, a correctness-sized configuration, so a rate without a roofline
+    (launch latency bounds it)."""
+    w = synth.TINY_E4M3
+    ht, tm, tables, layers, host = device_inputs(w, torch, E, G)
+    T = w.prompt
+    d_ids = torch.from_numpy(G.token_ids(w).astype(np.int32)).cuda()
+    h = torch.from_numpy(G.highway(w, T)).cuda()
+    ctx = make_ctx(E, w, tables, layers, T, T * (reps + 3))
+    stream = torch.cuda.current_stream()
+
+    def forward():                    # the same 64 tokens again, at the next positions
+        for l in range(w.n_layers):
+            ctx.forward(l, d_ids, T, h)
+
+    for _ in range(3):
+        forward()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        forward()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    ctx.check()
+    del ctx
+    return dict(workload=w.name, T=T, layers=w.n_layers, forwards=reps, ms_per_forward=ms,
+                value=T * w.n_layers / (ms / 1e3), unit="engram tokens/s per layer",
+                note="correctness-sized: launch latency bounds it, no roofline claim")
+
+
 def bench_gather_stress(args, torch, E, G, synth):
     """The large-table workload (one Q2_K layer of ~71 M rows, 5.9 GB; T
     16384 uniform tokens, so every row read is a random 84-byte block):
@@ -689,6 +722,9 @@ def main():
     if pre:
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
     stress = split = None
+    tiny = None if args.no_prefill else bench_tiny(args, torch, E, G, synth)
+    if tiny:
+        log(f"tiny: {tiny['ms_per_forward'] * 1e3:.1f} us a forward of {tiny['T']} tokens")
     if not args.no_prefill:
         stress = bench_gather_stress(args, torch, E, G, synth)
         log(f"gather stress: {stress['ms_per_step']:.3f} ms/step, gather "
@@ -754,6 +790,7 @@ def main():
             "stages_ms_per_layer_step": host_dec["stages"]},
         "decode_batched": batched,
         "prefill": pre,
+        "tiny_e4m3": tiny,
         "gather_stress": stress,
         "split_e4m3": split,
         "cpu_baseline": cpu,
