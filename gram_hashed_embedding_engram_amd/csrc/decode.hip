@@ -24,8 +24,16 @@
 // would have left there.
 //
 // With wkv registered as Q2_K blocks the projection loop is wkv_q2k.h's row
-// dot product instead (41 MB a layer instead of 252 MB): after the prologue
-// each lane copies its sub-blocks' activations from LDS into registers.
+// dot product instead (41 MB a layer instead of 252 MB), reading the
+// activations from LDS per sub-block.  With an e4m3 table (256-byte rows, too
+// large to stage through scalar registers) the table loads are vector loads
+// issued ahead of the first weight row, so waiting for them leaves the row in
+// flight.  The several-sequence kernel below does the same for 2-4 tokens,
+// one per sequence, in one pass over wkv.
+//
+// The step's position is a kernel argument, or -- for steps replayed from a
+// captured graph -- a device word that the step's last gate advances
+// (step_pos); either way it is checked against the history's length.
 //
 // The gate stays a launch of its own.  It needs every kv row, and doing it
 // in the last workgroup to finish was measured slower: the completion count
