@@ -740,7 +740,8 @@ def main():
     gbps = dec["proj_bytes"] / (dec["proj_avg_ms"] / 1e3) / 1e9
     staged_gbps = staged["proj_bytes"] / (staged["proj_avg_ms"] / 1e3) / 1e9
     out = {
-        "metric": "engram tokens/s per layer (decode T=1)",
+        "metric": "engram tokens/s per layer (decode T=1, prefill T=4096) + % HBM/MFMA roofline",
+        "value_is": "decode T=1 on the decode workload (prefill T=4096: the prefill entry)",
         "value": dec["value"],
         "unit": "engram tokens/s per layer",
         "n_gpus": 1,
