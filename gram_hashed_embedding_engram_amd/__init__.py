@@ -66,6 +66,7 @@ class ConfigC(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 6           # ENGRAM_ABI_VERSION of include/engram.h this binding follows
 
 
 def lib():
@@ -111,6 +112,10 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.engram_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.engram_abi_version()}, this "
+                               f"binding {ABI_VERSION}: rebuild it (python -m "
+                               "gram_hashed_embedding_engram_amd.build)")
         _lib = L
     return _lib
 

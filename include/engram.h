@@ -64,7 +64,11 @@ extern "C" {
  * "engram_v41.rs", ENGRAM_ROW_BYTES and module doc stage 2). */
 #define ENGRAM_Q2K_ROW_BYTES 84
 
+/* The message of the calling thread's last refused or failed call ("" if
+ * none); valid until that thread's next failing call. */
 const char *engram_last_error(void);
+/* ENGRAM_ABI_VERSION of the built library: a binding checks it against the
+ * header it was written for. */
 int32_t engram_abi_version(void);
 
 /* ------------------------------------------------------------------ hash */
@@ -369,6 +373,9 @@ int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage /*[4]*/,
  *   timing on, or with the one-launch decode kernels off. */
 int32_t engram_ctx_set_graph_mode(engram_ctx *ctx, int32_t enable, void *stream);
 
+/* Frees the context's host bookkeeping and its timing events (NULL: no-op).
+ * The workspace stays the caller's; work already enqueued on it is not
+ * waited for, so destroy a context only after its stream has finished. */
 void engram_ctx_destroy(engram_ctx *ctx);
 
 /* ------------------------------------------------------------ measurement */

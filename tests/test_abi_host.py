@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 6
+    assert L.engram_abi_version() == 6 == E.ABI_VERSION
+    assert "#define ENGRAM_ABI_VERSION %d" % E.ABI_VERSION in open(HEADER).read()
 
 
 def tables_c(nl=2, ng=4, nh=8, vocab=1000, mult=None, primes=None, offsets=None):
