@@ -311,6 +311,25 @@ def test_project_gemm_full_shape(E, decode, M):
     check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
 
 
+def test_project_run_twice_bit_identical(E, decode):
+    """Every projection kernel is deterministic: the same call twice gives
+    the same bits, at the token counts that select each kernel (one-token
+    GEMV, multi-token GEMV, few-token GEMM, tiled GEMM with a ragged tail and
+    at the prefill shape)."""
+    rng = np.random.default_rng(11)
+    w = decode.wkv[1]
+    for T in (1, 3, 8, 64, 300, 4096):
+        x = cuda(bf16_rand(rng, (T, 6144), 0.5))
+        ys = []
+        for _ in range(2):
+            y = torch.full((T, 20480), 0x7FC0, dtype=torch.int16, device="cuda")
+            E.project(x, w, y)
+            ys.append(y)
+        torch.cuda.synchronize()
+        log(f"project twice: T={T}")
+        assert torch.equal(ys[0], ys[1]), f"T={T}"
+
+
 # ---------------------------------------------- projection off Q2_K wkv
 def q2k_blocks(rng, n_out, nb):
     """Random Q2_K weight blocks [n_out, nb, 84] with fp16 d, dmin in the
