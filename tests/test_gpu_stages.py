@@ -150,6 +150,27 @@ def test_hash_bad_token_ids(E, tiny):
     np.testing.assert_array_equal(got, tiny.oracle_hasher(64).hash(subst, 0))
 
 
+def test_hash_degenerate_windows(E, tiny):
+    """Degenerate n-gram windows, bit for bit against the oracle: every token
+    unmapped (every window blocked at once), every token the pad token, and
+    unmapped tokens every third position (windows blocked part way)."""
+    tm = tiny.ht["token_map"]
+    unmapped = np.nonzero(tm == -1)[0]
+    mapped = np.nonzero(tm >= 0)[0]
+    rng = np.random.default_rng(5)
+    cases = {
+        "all unmapped": rng.choice(unmapped, size=48),
+        "all pad": np.zeros(48, dtype=np.int64),
+        "every third unmapped": np.where(np.arange(48) % 3 == 1, rng.choice(unmapped, size=48),
+                                         rng.choice(mapped, size=48)),
+    }
+    for name, ids in cases.items():
+        hist = torch.zeros(64, dtype=torch.int64, device="cuda")
+        got, err = run_hash(E, tiny, ids.astype(np.int32), 0, hist)
+        assert err == 0, name
+        np.testing.assert_array_equal(got, tiny.oracle_hasher(64).hash(ids, 0), err_msg=name)
+
+
 def test_hash_start_pos_and_empty(E, tiny):
     ids = G.token_ids(tiny.w)[:10]
     hist = torch.zeros(64, dtype=torch.int64, device="cuda")
@@ -470,6 +491,36 @@ def test_gate(E, T, hc, dim):
     d_h = torch.from_numpy(h).cuda()
     E.gate_apply(d_h, cuda(kv0.reshape(T, -1)), d_qk, 1e-6)
     np.testing.assert_array_equal(d_h.cpu().numpy().view(np.uint32), h.view(np.uint32))
+
+
+def test_gate_degenerate_rows(E):
+    """The gate's degenerate inputs against the oracle: a zero highway row
+    (h.h = 0, the eps floor sets the norm), a zero key (key.key = 0), a key
+    orthogonal to h.qk (the dot 0: the signed square root's 1e-6 clamp decides
+    the gate), and huge values (1e30, squares overflow to inf in f32)."""
+    import oracle
+    hc, dim, T = 4, 256, 4
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((T, hc, dim)).astype(np.float32)
+    kv = bf16_rand(rng, (T, hc + 1, dim), 0.5)
+    h[0, 1] = 0.0                                   # zero highway row
+    kv[1, 2] = 0                                    # zero key
+    kv[2, 0, ::2] = 0                               # key on odd positions ...
+    h[2, 0, 1::2] = 0.0                             # ... h on even ones: dot = 0
+    h[3, 3] = np.float32(1e30)                      # squares overflow
+    q = np.full((hc, dim), 0x3F80, dtype=np.uint16)  # q = k = 1
+    d_qk = torch.empty(hc, dim, dtype=torch.float32, device="cuda")
+    E.qk_product(cuda(q), cuda(q), d_qk)
+    d_h = torch.from_numpy(h).cuda()
+    E.gate_apply(d_h, cuda(kv.reshape(T, -1)), d_qk, 1e-6)
+    got = d_h.cpu().numpy()
+    want = oracle.gate_and_add(h, kv.reshape(T, -1), q, q, 1e-6)
+    finite = np.isfinite(want)
+    np.testing.assert_array_equal(np.isfinite(got), finite)
+    rows = [(0, 1), (1, 2), (2, 0)]
+    for t, c in rows:
+        e = relerr(got[t, c], want[t, c])
+        assert e <= 2e-3, f"row {(t, c)}: relerr {e:.2e}"
 
 
 @pytest.mark.parametrize("dim", [4096, 9216])
