@@ -45,15 +45,17 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h)
 }
 
 // e4m3fn code -> f32, from the format: sign, 4 exponent bits (bias 7), 3
-// mantissa bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
+// mantissa bits; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN, the
+// positive quiet NaN for either sign (metrale "deepseek_v41_ref/engram.rs",
+// e4m3_to_f32, returns f32::NAN for both codes).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c)
 {
     const uint32_t sign = (c & 0x80u) << 24;
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
     if (e == 0)
         return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
-    if (e == 15 && m == 7)
-        return __uint_as_float(0x7FC00000u | sign);
+    if (e == 15 && m == 7)              // both NaN codes: the positive quiet NaN
+        return __uint_as_float(0x7FC00000u);
     return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
 }
 

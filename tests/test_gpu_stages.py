@@ -223,6 +223,27 @@ def test_gather_every_tiny_row(E, tiny):
     np.testing.assert_array_equal(got, tiny.oracle_rows(0, ids))
 
 
+def test_gather_e4m3_every_code(E):
+    """Every e4m3 code (subnormals, signed zeros, the largest values and both
+    NaN codes) under power-of-two scales 2^0 .. 2^-4 and scale blocks of 128
+    and 16, gathered bit for bit as the oracle decodes them."""
+    import oracle
+    codes = np.tile(np.arange(256, dtype=np.uint8), (5, 1))          # row r: all codes
+    for sb in (128, 16):
+        nb = 256 // sb
+        scales = np.array([[2.0 ** -((r + j) % 5) for j in range(nb)] for r in range(5)],
+                          dtype=np.float32)
+        tab = E.Table(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                      head_dim=256, scale_block=sb)
+        ids = np.array([[4, 0, 3], [1, 2, 4]], dtype=np.int64)
+        rows = torch.empty(6, 256, dtype=torch.int16, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        E.gather_dequant(tab, cuda(ids), 2, 3, 3, rows, err)
+        assert int(err.item()) == 0
+        want = oracle.gather(codes, scales, ids, 256, sb)
+        np.testing.assert_array_equal(to_np_u16(rows), want, err_msg=f"scale block {sb}")
+
+
 def test_gather_bad_row_ids(E, tiny, decode):
     for dev in (tiny, decode):
         n = dev.layers[0]["rows"]
