@@ -171,6 +171,32 @@ def test_hash_degenerate_windows(E, tiny):
         np.testing.assert_array_equal(got, tiny.oracle_hasher(64).hash(ids, 0), err_msg=name)
 
 
+def test_hash_large_moduli(E, tiny):
+    """The 64-bit hash at the extremes of its arithmetic, bit for bit against
+    the oracle: multipliers near 2^63 (the wrapping products use every bit),
+    moduli from 2^31 - 1 up to 2^62 - 57 (the remainder of a full 64-bit
+    value), the offsets' upper bound, and a long window (n-gram 8)."""
+    import oracle
+    tm_host = tiny.ht["token_map"]
+    tm = torch.from_numpy(tm_host).cuda()
+    for ng, nh in ((3, 2), (8, 1)):
+        cols = (ng - 1) * nh
+        rng = np.random.default_rng(ng)
+        mult = ((rng.integers(2**62, 2**63 - 1, size=(1, ng), dtype=np.int64)) | 1)
+        moduli = np.array([2**61 - 1, 2**31 - 1, 4294967291, 2**62 - 57, 1000000007,
+                           2**40 + 15, 3, 2**62 - 1][:cols], dtype=np.int64).reshape(1, cols)
+        offsets = (2**62 - moduli).reshape(1, cols)            # the largest allowed
+        offsets[0, ::2] = np.arange(0, cols, 2)
+        tables = E.HashTables(tm, tiny.ht["pad_id"], mult, moduli, offsets)
+        ids = G.token_ids(tiny.w)[:40]
+        hist = torch.zeros(64, dtype=torch.int64, device="cuda")
+        out = torch.empty(40, 1, cols, dtype=torch.int64, device="cuda")
+        E.hash(tables, cuda(ids.astype(np.int32)), 0, hist, out)
+        want = oracle.Hasher(tm_host, tiny.ht["pad_id"], mult, moduli, offsets, 64).hash(ids, 0)
+        np.testing.assert_array_equal(out.cpu().numpy(), want, err_msg=f"n-gram {ng}")
+        assert (want >= 0).all() and (want < 2**62).all()
+
+
 def test_hash_start_pos_and_empty(E, tiny):
     ids = G.token_ids(tiny.w)[:10]
     hist = torch.zeros(64, dtype=torch.int64, device="cuda")
