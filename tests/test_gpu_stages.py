@@ -367,6 +367,20 @@ def test_project_gemm_tiny_shape(E, tiny, M):
     check_project(E, x, tiny.wkv[0], tiny.layers[0]["wkv"])
 
 
+@pytest.mark.parametrize("M,K,N", [(300, 64, 336), (257, 128, 16), (600, 192, 656),
+                                   (5, 64, 32), (2, 64, 48), (1, 64, 16)])
+def test_project_short_k(E, M, K, N):
+    """The shortest contractions (K = 64..192: fewer K tiles than the GEMM's
+    pipeline stages, so its prefetch runs past the end and reloads the last
+    tile) at ragged M and N, on every projection kernel the token count
+    selects, against the oracle."""
+    rng = np.random.default_rng(M + K + N)
+    x = bf16_rand(rng, (M, K), 0.5)
+    w = bf16_rand(rng, (N, K), 0.05)
+    log(f"project short K: M={M} K={K} N={N}")
+    check_project(E, x, cuda(w), w)
+
+
 @pytest.mark.parametrize("M", [32, 4096])
 def test_project_gemm_full_shape(E, decode, M):
     rng = np.random.default_rng(7 + M)
