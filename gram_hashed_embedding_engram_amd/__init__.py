@@ -138,6 +138,29 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _room(t):
+    """Bytes from a tensor's (or array's) first element to the end of its
+    storage: what a kernel may touch through its address."""
+    if isinstance(t, np.ndarray):
+        return t.nbytes if t.flags.c_contiguous else -1
+    return t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+
+
+def _need(t, name, nbytes, dense=True):
+    """Refuse, before the library sees the address, a tensor that a call of
+    these sizes would read or write past the end of its storage, or a strided
+    view where the kernel takes rows to be back to back.  The C entry points
+    cannot see a buffer's size; the binding can."""
+    if t is None:
+        return
+    if dense and not isinstance(t, np.ndarray) and not t.is_contiguous():
+        raise EngramError(E_ARG, f"{name}: a contiguous tensor is needed")
+    room = _room(t)
+    if nbytes > room:
+        raise EngramError(E_ARG, f"{name}: the call needs {nbytes} bytes, its storage holds "
+                                 f"{max(room, 0)} from this address")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -192,6 +215,11 @@ class Table:
 
 
 def hash(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err=None, stream=None):
+    T = int(d_ids.numel())
+    _need(d_ids, "ids", 4 * T)
+    _need(d_history, "history", 8 * int(d_history.numel()))
+    _need(d_row_ids, "row_ids", 8 * T * tables.n_layers * tables.cols)
+    _need(d_err, "err", 4)
     _check(lib().engram_hash(ctypes.byref(tables.c), _ptr(d_ids), int(d_ids.numel()),
                              int(start_pos), _ptr(d_history), int(d_history.numel()),
                              _ptr(d_row_ids), _ptr(d_err), _stream(stream)))
@@ -201,6 +229,10 @@ def hash_batch(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err
                stream=None):
     """d_ids [B, T] int32, d_history [B, max_seq] int64, d_row_ids [B*T, nl, cols]."""
     B, T = d_ids.shape
+    _need(d_ids, "ids", 4 * B * T)
+    _need(d_history, "history", 8 * B * d_history.shape[1])
+    _need(d_row_ids, "row_ids", 8 * B * T * tables.n_layers * tables.cols)
+    _need(d_err, "err", 4)
     _check(lib().engram_hash_batch(ctypes.byref(tables.c), _ptr(d_ids), int(B), int(T),
                                    int(start_pos), _ptr(d_history), int(d_history.shape[1]),
                                    _ptr(d_row_ids), _ptr(d_err), _stream(stream)))
@@ -208,6 +240,11 @@ def hash_batch(tables: HashTables, d_ids, start_pos, d_history, d_row_ids, d_err
 
 def gather_dequant(table: Table, d_row_ids, T, cols, id_stride, d_rows, d_err=None,
                    stream=None):
+    if T > 0:
+        # ids of token t at d_row_ids + t*id_stride: any view that reaches them will do
+        _need(d_row_ids, "row_ids", 8 * ((T - 1) * id_stride + cols), dense=False)
+        _need(d_rows, "rows", 2 * T * cols * table.c.head_dim)
+    _need(d_err, "err", 4)
     _check(lib().engram_gather_dequant(ctypes.byref(table.c), _ptr(d_row_ids), int(T),
                                        int(cols), int(id_stride), _ptr(d_rows), _ptr(d_err),
                                        _stream(stream)))
@@ -216,6 +253,9 @@ def gather_dequant(table: Table, d_row_ids, T, cols, id_stride, d_rows, d_err=No
 def project(d_x, d_w, d_y, stream=None):
     T, K = d_x.shape
     N = d_w.shape[0]
+    _need(d_x, "x", 2 * T * K)
+    _need(d_w, "w", 2 * N * K)
+    _need(d_y, "y", 2 * T * N)
     _check(lib().engram_project(_ptr(d_x), _ptr(d_w), _ptr(d_y), T, K, N, _stream(stream)))
 
 
@@ -223,16 +263,25 @@ def project_q2k(d_x, d_wq, d_y, stream=None):
     """d_x [T, K] bf16 bits (T <= 1), d_wq [N, K/256, 84] uint8 Q2_K blocks."""
     T, K = d_x.shape
     N = d_wq.shape[0]
+    _need(d_x, "x", 2 * T * K)
+    _need(d_wq, "wkv_q2k", N * (K // 256) * 84)
+    _need(d_y, "y", 2 * T * N)
     _check(lib().engram_project_q2k(_ptr(d_x), _ptr(d_wq), _ptr(d_y), T, K, N, _stream(stream)))
 
 
 def dequant_q2k(d_blocks, d_out, stream=None):
     """Q2_K blocks (any shape [..., 84] uint8) -> d_out [n_blocks * 256] bf16 bits."""
     n = d_blocks.numel() // 84
+    _need(d_blocks, "blocks", 84 * n)
+    _need(d_out, "out", 2 * 256 * n)
     _check(lib().engram_dequant_q2k(_ptr(d_blocks), n, _ptr(d_out), _stream(stream)))
 
 
 def qk_product(d_q, d_k, d_qk, stream=None):
+    n = int(d_q.numel())
+    _need(d_q, "q", 2 * n)
+    _need(d_k, "k", 2 * n)
+    _need(d_qk, "qk", 4 * n)
     _check(lib().engram_qk_product(_ptr(d_q), _ptr(d_k), _ptr(d_qk), int(d_q.numel()),
                                    _stream(stream)))
 
@@ -240,12 +289,16 @@ def qk_product(d_q, d_k, d_qk, stream=None):
 def stream_read(d_src, d_sink, stream=None):
     """Stream d_src once, one XOR fold per wavefront into d_sink [8192]
     int32 (the read-rate yardstick; engram_stream_read)."""
+    _need(d_sink, "sink", 4 * STREAM_SINK_WORDS)
     _check(lib().engram_stream_read(_ptr(d_src), int(d_src.numel() * d_src.element_size()),
                                     _ptr(d_sink), _stream(stream)))
 
 
 def gate_apply(d_h, d_kv, d_qk, eps, stream=None):
     T, hc, dim = d_h.shape
+    _need(d_h, "h", 4 * T * hc * dim)
+    _need(d_kv, "kv", 2 * T * dim * (hc + 1))
+    _need(d_qk, "qk", 4 * hc * dim)
     _check(lib().engram_gate_apply(_ptr(d_h), _ptr(d_kv), _ptr(d_qk), T, hc, dim,
                                    float(eps), _stream(stream)))
 
@@ -274,6 +327,9 @@ class Context:
         self._keep = {}
 
     def add_layer(self, hash_index, table: Table, d_wkv, d_qk):
+        K = self.cols * self.head_dim
+        _need(d_wkv, "wkv", 2 * self.dim * (self.hc + 1) * K)
+        _need(d_qk, "qk", 4 * self.hc * self.dim)
         self._keep[hash_index] = (table, d_wkv, d_qk)
         _check(lib().engram_ctx_add_layer(self.h, hash_index, ctypes.byref(table.c),
                                           _ptr(d_wkv), _ptr(d_qk)))
@@ -281,6 +337,8 @@ class Context:
     def set_wkv_q2k(self, hash_index, d_wq):
         """Registers (or, with None, drops) the layer's wkv as Q2_K blocks."""
         table, wkv, qk = self._keep[hash_index][:3]
+        N, K = self.dim * (self.hc + 1), self.cols * self.head_dim
+        _need(d_wq, "wkv_q2k", N * (K // 256) * 84)
         self._keep[hash_index] = (table, wkv, qk, d_wq)
         _check(lib().engram_ctx_set_wkv_q2k(self.h, hash_index, _ptr(d_wq)))
 
@@ -288,6 +346,9 @@ class Context:
         _check(lib().engram_reset(self.h, _stream(stream)))
 
     def forward(self, hash_index, d_ids, T, d_h, stream=None):
+        M = self.batch * int(T)
+        _need(d_ids, "ids", 4 * M)
+        _need(d_h, "h", 4 * M * self.hc * self.dim)
         _check(lib().engram_forward(self.h, hash_index, _ptr(d_ids), int(T), _ptr(d_h),
                                     _stream(stream)))
 

@@ -304,3 +304,51 @@ def test_binding_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(E, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         E.lib()
+
+
+def test_binding_refuses_short_buffers(monkeypatch):
+    """The C entry points cannot see a buffer's size; the binding refuses a
+    tensor that a call of the given sizes would read or write past the end of
+    its storage (or a strided view where rows must be dense) before the
+    library is reached."""
+    torch = pytest.importorskip("torch")
+
+    def unreachable():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(E, "lib", unreachable)
+    i16 = lambda *s: torch.zeros(*s, dtype=torch.int16)
+
+    def refused(f, *args, what):
+        with pytest.raises(E.EngramError, match=what) as e:
+            f(*args, stream=0)
+        assert e.value.code == E.E_ARG
+
+    refused(E.project, i16(4, 64), i16(32, 32), i16(4, 32), what="w: the call needs 4096 bytes")
+    refused(E.project, i16(4, 64), i16(32, 64), i16(4, 16), what="y: the call needs 256 bytes")
+    refused(E.project, i16(64, 4).t(), i16(32, 64), i16(4, 32), what="x: a contiguous tensor")
+    refused(E.project_q2k, i16(1, 512), torch.zeros(16, 1, 84, dtype=torch.uint8), i16(1, 16),
+            what="wkv_q2k: the call needs 2688 bytes")
+    refused(E.dequant_q2k, torch.zeros(3 * 84, dtype=torch.uint8), i16(2 * 256), what="out")
+    refused(E.gate_apply, torch.zeros(2, 4, 256), i16(2, 256 * 4), torch.zeros(4, 256), 1e-6,
+            what="kv: the call needs 5120 bytes")
+    refused(E.qk_product, i16(4, 256), i16(4, 256), torch.zeros(4, 128),
+            what="qk: the call needs 4096 bytes")
+    refused(E.qk_product, i16(4, 256), i16(2, 256), torch.zeros(4, 256),
+            what="k: the call needs 2048 bytes")
+    refused(E.stream_read, torch.zeros(4096, dtype=torch.uint8),
+            torch.zeros(100, dtype=torch.int32), what="sink")
+
+    tabs = E.HashTables(torch.zeros(16, dtype=torch.int64), 0, np.ones((2, 3), np.int64),
+                        np.full((2, 4), 7, np.int64), np.zeros((2, 4), np.int64))
+    ids = torch.zeros(5, dtype=torch.int32)
+    hist = torch.zeros(16, dtype=torch.int64)
+    refused(E.hash, tabs, ids, 0, hist, torch.zeros(5, 2, 3, dtype=torch.int64),
+            what="row_ids: the call needs 320 bytes")
+    # a strided id view reaching every id passes the check; one that stops short does not
+    table = E.Table.__new__(E.Table)          # device table stand-in (no host mapping)
+    table.c = E.TableC(E.FMT_Q2K, 256, 0, 0, 64, FAKE, None)
+    ids2 = torch.zeros(5, 8, dtype=torch.int64)
+    refused(E.gather_dequant, table, ids2[1:, 4:], 5, 4, 8, i16(5, 4 * 256),
+            what="row_ids: the call needs 288 bytes, its storage holds 224")
+    with pytest.raises(AssertionError, match="library was reached"):
+        E.gather_dequant(table, ids2[:, 4:], 5, 4, 8, i16(5, 4 * 256), stream=0)
