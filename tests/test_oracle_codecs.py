@@ -264,3 +264,87 @@ def test_project_q2k_contracts_over_inputs(orc):
         x[0, k] = 1.0
         y = orc.project_q2k(torch_bf16_bits(x).reshape(1, -1), blocks)
         np.testing.assert_array_equal(y[0], w[:, k])
+
+
+# ------------------------------------------- gather by id (which row, which scales)
+def _id_patterns(n_rows, rng):
+    """Ids that a gather reading row i instead of row ids[i] (or the scales of
+    row i) cannot satisfy: a permutation, repeats, a descending run, the
+    first and the last row, and a 2-D shape."""
+    perm = rng.permutation(n_rows)
+    return [perm,
+            np.array([n_rows - 1, 0, n_rows - 1, 5, 5, 5, 2]),
+            np.arange(n_rows - 1, -1, -1),
+            rng.integers(0, n_rows, size=(3, 7)),
+            np.array([n_rows - 1])]
+
+
+def test_gather_q2k_selects_rows_by_id(orc):
+    """oracle.gather row i is the decode of table row ids[i] (metrale
+    "deepseek_v41_ref/engram.rs", embed_rows: rows selected by hash id from
+    the dequantised table; atlascybernetics "engram_v41.rs", rows_from_q2k).
+    Every table row differs (random bytes, distinct fp16 d/dmin per row), and
+    the expected rows come from the second, streaming-order decoder."""
+    rng = np.random.default_rng(21)
+    n_rows = 37
+    table = rng.integers(0, 256, size=(n_rows, 84)).astype(np.uint8)
+    dd = (np.arange(2 * n_rows, dtype=np.float64) * 1e-4 + 1e-3).reshape(n_rows, 2)
+    table[:, 80:84] = dd.astype(np.float16).view(np.uint8).reshape(n_rows, 4)
+    want_rows = np.stack([decode_q2k_stream(table[r]) for r in range(n_rows)])
+    assert len({r.tobytes() for r in want_rows}) == n_rows
+    for ids in _id_patterns(n_rows, rng):
+        got = orc.gather(table, None, ids)
+        np.testing.assert_array_equal(got, want_rows[np.asarray(ids).ravel()])
+
+
+def test_gather_q2k_rows_carry_their_index(orc):
+    """Designed table: row r has zero quants, scale 0, every min nibble 1 and
+    dmin = (r + 1) / 64, so every value of row r is -(r + 1) / 64, exact in
+    bf16; the gathered values name the row that was read."""
+    n_rows = 64
+    table = np.stack([encode_q2k(np.zeros(256, int), np.zeros(16, int), np.ones(16, int),
+                                 0.0, (r + 1) / 64) for r in range(n_rows)])
+    ids = np.array([63, 0, 17, 17, 42, 1, 62, 63])
+    got = orc.f32_from_bf16(orc.gather(table, None, ids))
+    want = np.repeat((-(ids + 1) / 64).astype(np.float32)[:, None], 256, axis=1)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_gather_e4m3_selects_codes_and_scales_by_id(orc):
+    """oracle.gather of an e4m3 table: row i is the codes of row ids[i] times
+    that row's own block scales (metrale "deepseek_v41_ref/engram.rs",
+    regen_table: a row's values times its block's scale; embed_rows: rows
+    selected by id).  Codes differ per row and the scales differ per row and
+    per block (2^k, k in [-4, 0]); expected values come from torch's e4m3fn
+    decode times the scale, in float64 (exact in bf16)."""
+    rng = np.random.default_rng(22)
+    for head_dim, block in ((256, 128), (256, 16), (64, 32)):
+        n_rows = 29
+        nb = head_dim // block
+        codes = rng.integers(0, 256, size=(n_rows, head_dim)).astype(np.uint8)
+        codes[codes == 0x7F] = 0x7E
+        codes[codes == 0xFF] = 0xFE
+        k = rng.integers(-4, 1, size=(n_rows, nb))
+        k[np.arange(n_rows), np.arange(n_rows) % nb] = -(np.arange(n_rows) % 5)
+        scales = np.ldexp(1.0, k).astype(np.float32)
+        dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+        full = dec * np.repeat(scales.astype(np.float64), block, axis=1)
+        for ids in _id_patterns(n_rows, rng):
+            flat = np.asarray(ids).ravel()
+            got = orc.gather(codes, scales, ids, head_dim, block)
+            np.testing.assert_array_equal(orc.f32_from_bf16(got).astype(np.float64), full[flat])
+
+
+def test_gather_e4m3_scales_name_the_row(orc):
+    """Designed e4m3 table: every code is 1.0 (0x38) and row r's scales are
+    2^-(r % 5) in block 0 and 2^-((r + 2) % 5) in block 1, so each gathered
+    half-row shows which row's scales were applied."""
+    n_rows, head_dim, block = 10, 256, 128
+    codes = np.full((n_rows, head_dim), 0x38, dtype=np.uint8)
+    r = np.arange(n_rows)
+    scales = np.stack([np.ldexp(1.0, -(r % 5)), np.ldexp(1.0, -((r + 2) % 5))],
+                      axis=1).astype(np.float32)
+    ids = np.array([9, 3, 3, 0, 7])
+    got = orc.f32_from_bf16(orc.gather(codes, scales, ids, head_dim, block))
+    np.testing.assert_array_equal(got[:, :128], np.repeat(scales[ids, :1], 128, axis=1))
+    np.testing.assert_array_equal(got[:, 128:], np.repeat(scales[ids, 1:], 128, axis=1))
