@@ -95,30 +95,36 @@ float orc_e4m3_to_f32(uint8_t b)
     return sign * (1.0f + m / 8.0f) * ldexpf(1.0f, e - 7);
 }
 
-/* f32 -> e4m3fn, round to nearest even ([metrale] `f32_to_e4m3_rne`): NaN
- * gives 0x7F, anything above 448 saturates to 0x7E, f32 subnormals give a
- * signed zero, below 2^-6 the e4m3 subnormal grid of step 2^-9 is used. */
+/* f32 -> e4m3fn code, written from the format itself ([metrale]
+ * `f32_to_e4m3_rne` is the saturating, round-to-nearest-even encoder the
+ * pages use).  Codes 0x00..0x7E are the non-negative finite e4m3fn values in
+ * increasing order (0x7F is NaN), so the magnitude's code is the one whose
+ * value lies nearest |x|; exactly half-way between two neighbours the even
+ * code wins.  Magnitudes at or past the largest finite value, 448 (0x7E),
+ * including infinity, take 0x7E; NaN takes 0x7F; the sign bit is copied. */
 uint8_t orc_f32_to_e4m3_rne(float x)
 {
     if (isnan(x))
         return 0x7F;
-    uint8_t sign = signbit(x) ? 0x80 : 0;
-    uint32_t bits = f32_bits(fabsf(x));
-    int exp_field = (int)((bits >> 23) & 0xFF);
-    if (exp_field == 0)
-        return sign;
-    double a = fabs((double)x);
-    if (a > 448.0)
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs((double)x);
+    int below = 0;                         /* the largest code whose value <= a */
+    for (int c = 1; c <= 0x7E; c++)
+        if ((double)orc_e4m3_to_f32((uint8_t)c) <= a)
+            below = c;
+    if (below == 0x7E)
         return sign | 0x7E;
-    int e = exp_field - 127;
-    if (e < -6) {
-        /* m = 8 rounds up into the first normal, whose code is 0x08 */
-        double r = nearbyint(a * 512.0);        /* default rounding: ties to even */
-        return sign | (uint8_t)r;
-    }
-    int mant = (int)nearbyint((a * ldexp(1.0, -e) - 1.0) * 8.0);
-    if (mant == 8) { e += 1; mant = 0; }
-    return sign | (uint8_t)(((e + 7) << 3) | mant);
+    /* both neighbours and their midpoint are exact in double */
+    const double half_way = 0.5 * ((double)orc_e4m3_to_f32((uint8_t)below) +
+                                   (double)orc_e4m3_to_f32((uint8_t)(below + 1)));
+    int code;
+    if (a < half_way)
+        code = below;
+    else if (a > half_way)
+        code = below + 1;
+    else
+        code = (below & 1) ? below + 1 : below;
+    return sign | (uint8_t)code;
 }
 
 /* ------------------------------------------------------------ 1. the hash */
@@ -293,6 +299,39 @@ void orc_linear_bf16(const uint16_t *x, int64_t rows, int64_t in_f, const uint16
 
 /* ----------------------------------------------------------- 4. the gate */
 
+/* The three f32 sums a gate row needs, accumulated in index order: the
+ * highway's energy h.h, the key's energy key.key and the weighted product
+ * sum (h * qk) * key, where qk, the gate weight, is the f32 product of the
+ * two bf16 weights q and k ([atlas] `upload_qk`). */
+static void gate_sums(const float *h, const uint16_t *key, const uint16_t *q_w,
+                      const uint16_t *k_w, int64_t dim, float *hh, float *kk, float *dot)
+{
+    float s_hh = 0.0f, s_kk = 0.0f, s_dot = 0.0f;
+    for (int64_t d = 0; d < dim; d++) {
+        const float kd = orc_f32_from_bf16(key[d]);
+        const float weight = orc_f32_from_bf16(q_w[d]) * orc_f32_from_bf16(k_w[d]);
+        s_hh += h[d] * h[d];
+        s_kk += kd * kd;
+        s_dot += h[d] * weight * kd;
+    }
+    *hh = s_hh;
+    *kk = s_kk;
+    *dot = s_dot;
+}
+
+/* The gate of one row ([metrale] `gate_and_add`): the weighted product sum
+ * scaled by the reciprocal rms of h and of the key (each with eps under the
+ * root) and by 1/sqrt(dim); the square root of that score's magnitude, not
+ * taken below 1e-6, carries the score's sign into a logistic sigmoid. */
+static float gate_scalar(float hh, float kk, float dot, int64_t dim, float eps)
+{
+    const float fdim = (float)dim;
+    const float norm = (1.0f / sqrtf(hh / fdim + eps)) * (1.0f / sqrtf(kk / fdim + eps));
+    const float score = dot * norm * powf(fdim, -0.5f);
+    const float root = sqrtf(fmaxf(fabsf(score), 1e-6f));
+    return 1.0f / (1.0f + expf(-copysignf(root, score)));
+}
+
 typedef struct {
     float *h;
     const uint16_t *kv, *q_w, *k_w;
@@ -301,35 +340,22 @@ typedef struct {
     int round_bf16;
 } gate_job;
 
+/* Tokens t0..t1-1: for each stream, its gate from the three sums, then
+ * h += gate * value in f32 (rounded to bf16 afterwards only under the flag). */
 static void *gate_worker(void *arg)
 {
     const gate_job *j = (const gate_job *)arg;
     const int64_t hc = j->hc, dim = j->dim, kv_w = dim * (hc + 1);
-    const float inv_sqrt_dim = powf((float)dim, -0.5f);
     for (int64_t t = j->t0; t < j->t1; t++) {
-        const uint16_t *value = j->kv + t * kv_w + hc * dim;
+        const uint16_t *kv_t = j->kv + t * kv_w;
+        const uint16_t *value = kv_t + hc * dim;
         for (int64_t c = 0; c < hc; c++) {
             float *h = j->h + (t * hc + c) * dim;
-            const uint16_t *key = j->kv + t * kv_w + c * dim;
-            float hh = 0.0f, kk = 0.0f, dot = 0.0f;
+            float hh, kk, dot;
+            gate_sums(h, kv_t + c * dim, j->q_w + c * dim, j->k_w + c * dim, dim, &hh, &kk, &dot);
+            const float gate = gate_scalar(hh, kk, dot, dim, j->eps);
             for (int64_t d = 0; d < dim; d++) {
-                float kd = orc_f32_from_bf16(key[d]);
-                /* q and k enter only as their product, an f32 product of two
-                 * bf16 values ([atlas] `upload_qk`) */
-                float qk = orc_f32_from_bf16(j->q_w[c * dim + d]) *
-                           orc_f32_from_bf16(j->k_w[c * dim + d]);
-                hh += h[d] * h[d];
-                kk += kd * kd;
-                dot += h[d] * qk * kd;
-            }
-            float rstd = (1.0f / sqrtf(hh / (float)dim + j->eps)) *
-                         (1.0f / sqrtf(kk / (float)dim + j->eps));
-            float s = dot * rstd * inv_sqrt_dim;
-            /* signed square root, magnitude floored at 1e-6, then sigmoid */
-            float g = copysignf(sqrtf(fmaxf(fabsf(s), 1e-6f)), s);
-            float gate = 1.0f / (1.0f + expf(-g));
-            for (int64_t d = 0; d < dim; d++) {
-                float y = h[d] + gate * orc_f32_from_bf16(value[d]);
+                const float y = h[d] + gate * orc_f32_from_bf16(value[d]);
                 h[d] = j->round_bf16 ? orc_f32_from_bf16(orc_bf16_from_f32(y)) : y;
             }
         }
