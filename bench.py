@@ -27,8 +27,10 @@ by its average event-timed duration.  `traffic` is read from the committed
 rocprofv3 counter summary when it matches the current kernel source, else
 null.
 
-The oracle (plain C on the host cores) is timed on a bounded sample of the
-same decode steps for `cpu_baseline`.
+The oracle (plain C on the host cores) is timed on bounded samples of the
+same workloads: the decode workload's first single-token steps (its own
+token stream and per-step highways) for `cpu_baseline`, and the prefill
+workload's first tokens for `prefill.cpu_baseline`.
 """
 import argparse
 import hashlib
@@ -404,6 +406,7 @@ def bench_prefill(args, torch, E, G, synth):
                       traffic=counter_traffic("gemm_prefill_T4096_counters.md", "gemm.hip")),
         gather_GBps=T * w.cols * (84 + 512 + 8) / (gather_ms / 1e3) / 1e9,
         gate_GBps=gate_bytes / (gate_ms / 1e3) / 1e9,
+        ht=ht, host=host,
     )
 
 
@@ -593,35 +596,88 @@ def read_ceiling(torch, E, synth, reps=30):
                 HBM_PEAK_GBPS)
 
 
-def cpu_baseline(res, synth, budget_s):
-    """The oracle on the host cores over the first decode steps (both
-    layers), until budget_s seconds of work have run."""
+def oracle_threads():
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when set (the share of a shared host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def layer_rows(oracle, w, L, rid):
+    """The oracle's gather of one layer's rows for row ids [T, cols]."""
+    return oracle.gather(L["table"], L["scales"], rid, w.head_dim, w.scale_block).reshape(
+        rid.shape[0], -1)
+
+
+def layer_wkv(oracle, L):
+    return L["wkv"] if L.get("wkv_q2k") is None else oracle.expand_q2k_matrix(L["wkv_q2k"])
+
+
+def cpu_baseline(w, ht, host, budget_s, max_steps=256, threads=None):
+    """The oracle on the host cores over the workload's decode: its prompt,
+    then single-token steps through every layer (hash, gather + dequant,
+    projection, gate of that step's own highway), until budget_s seconds of
+    steps have run or max_steps are done.  The token stream (prompt +
+    max_steps ids) and the per-step highways are the workload's own, drawn
+    here, so the sample does not depend on how many steps the GPU legs ran."""
     import oracle
-    w = synth.DECODE_Q2K
-    ht, host, ids = res["ht"], res["host"], res["ids"]
-    threads = oracle.default_threads()
+    from synth import generate as G
+    threads = threads or oracle_threads()
+    ids = G.token_ids(w, w.prompt + max_steps)
+    hw = G.highway(w, max_steps, decode=True)
+    wkv = [layer_wkv(oracle, L) for L in host]
     hasher = oracle.Hasher(ht["token_map"], ht["pad_id"], ht["multipliers"], ht["primes"],
                            ht["offsets"], ids.size)
     hasher.hash(ids[:w.prompt], 0)
-    h = np.random.default_rng(0).standard_normal((1, w.hc, w.dim)).astype(np.float32)
-    pos, steps = w.prompt, 0
+    pos, steps, el = w.prompt, 0, 0.0
     t0 = time.perf_counter()
-    while True:
+    while steps < max_steps and (steps == 0 or el < budget_s):
         rid = hasher.hash(ids[pos:pos + 1], pos)
+        h = hw[steps:steps + 1]
         for l in range(w.n_layers):
             L = host[l]
-            rows = oracle.gather(L["table"], None, rid[:, l, :]).reshape(1, -1)
-            kv = oracle.linear_bf16(rows, L["wkv"], nthreads=threads)
+            rows = layer_rows(oracle, w, L, rid[:, l, :])
+            kv = oracle.linear_bf16(rows, wkv[l], nthreads=threads)
             h = oracle.gate_and_add(h, kv, L["q"], L["k"], w.eps, nthreads=1)
         pos += 1
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 256:
-            break
     return dict(value=steps * w.n_layers / el, unit="engram tokens/s per layer", cores=threads,
-                kind="oracle",
-                sample=f"the first {steps} decode steps of {w.name} (both layers: hash, "
-                       f"gather, projection, gate), {el:.1f} s")
+                kind="oracle", steps=steps, seconds=el,
+                sample=f"the first {steps} single-token decode steps of {w.name} after its "
+                       f"{w.prompt}-token prompt, every layer (hash, gather + dequant, "
+                       f"projection, gate), {el:.1f} s")
+
+
+def cpu_baseline_prefill(w, ht, host, sample_tokens=64, threads=None):
+    """The oracle on the host cores over a bounded sample of the prefill
+    workload: its first sample_tokens tokens as one call through every layer
+    (one hash pass, then gather + dequant, projection and gate per layer).
+    The tokens and highway are the first rows of the workload's own."""
+    import oracle
+    from synth import generate as G
+    threads = threads or oracle_threads()
+    S = sample_tokens
+    ids = G.token_ids(w)[:S]
+    h = np.ascontiguousarray(G.highway(w, w.prompt)[:S])
+    wkv = [layer_wkv(oracle, L) for L in host]
+    t0 = time.perf_counter()
+    hasher = oracle.Hasher(ht["token_map"], ht["pad_id"], ht["multipliers"], ht["primes"],
+                           ht["offsets"], S)
+    rid = hasher.hash(ids, 0)
+    for l in range(w.n_layers):
+        L = host[l]
+        rows = layer_rows(oracle, w, L, rid[:, l, :])
+        kv = oracle.linear_bf16(rows, wkv[l], nthreads=threads)
+        h = oracle.gate_and_add(h, kv, L["q"], L["k"], w.eps, nthreads=threads)
+    el = time.perf_counter() - t0
+    return dict(value=S * w.n_layers / el, unit="engram tokens/s per layer", cores=threads,
+                kind="oracle", tokens=S, seconds=el,
+                sample=f"the first {S} of the {w.prompt} tokens of {w.name} as one call, every "
+                       f"layer (hash, gather + dequant, projection, gate), {el:.1f} s")
 
 
 def main():
@@ -633,7 +689,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the many-token legs (prefill, gather stress, e4m3 split)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle decode steps for cpu_baseline")
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=64,
+                    help="tokens of the prefill workload the oracle runs for "
+                         "prefill.cpu_baseline")
     ap.add_argument("--batch-sequences", type=int, nargs="*", default=[4],
                     help="also decode this many sequences together (one weight pass per step)")
     ap.add_argument("--no-decode", action="store_true",
@@ -676,7 +736,10 @@ def main():
                           "kernel": "torch.neg float32, 3 launches"}))
         return
     if args.no_decode:
-        print(json.dumps({"prefill": bench_prefill(args, torch, E, G, synth)}), flush=True)
+        pre = bench_prefill(args, torch, E, G, synth)
+        pre.pop("ht")
+        pre.pop("host")
+        print(json.dumps({"prefill": pre}), flush=True)
         return
     if args.only_stress:
         print(json.dumps({"gather_stress": bench_gather_stress(args, torch, E, G, synth)}),
@@ -735,7 +798,17 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
-        cpu = cpu_baseline(dec, synth, args.cpu_budget)
+        cpu = cpu_baseline(synth.DECODE_Q2K, dec["ht"], dec["host"], args.cpu_budget)
+        log(f"cpu baseline: {cpu['steps']} decode steps in {cpu['seconds']:.1f} s on "
+            f"{cpu['cores']} threads")
+        if pre:
+            pre["cpu_baseline"] = cpu_baseline_prefill(synth.PREFILL_Q2K, pre.pop("ht"),
+                                                       pre.pop("host"), args.cpu_prefill_tokens)
+            log(f"cpu baseline (prefill): {pre['cpu_baseline']['tokens']} tokens in "
+                f"{pre['cpu_baseline']['seconds']:.1f} s")
+    if pre:
+        pre.pop("ht", None)
+        pre.pop("host", None)
     w = synth.DECODE_Q2K
     gbps = dec["proj_bytes"] / (dec["proj_avg_ms"] / 1e3) / 1e9
     staged_gbps = staged["proj_bytes"] / (staged["proj_avg_ms"] / 1e3) / 1e9

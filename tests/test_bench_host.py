@@ -6,6 +6,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 import synth
 
@@ -52,3 +54,57 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "single MI355X" in r.stderr
+
+
+def test_cpu_baseline_runs_its_own_stream():
+    """The oracle leg draws its own prompt + max_steps token ids and per-step
+    highways, so it never runs out of tokens whatever --steps/--warmup the GPU
+    legs used (the driver's --steps 20 --warmup 5 gave those legs an 82-token
+    stream, and the leg once hashed an empty slice at its 51st step)."""
+    from synth import generate as G
+    w = synth.ODD_Q2K
+    ht = G.hash_tables(w)
+    host = [G.layer_inputs(w, ht, l) for l in range(w.n_layers)]
+    r = bench.cpu_baseline(w, ht, host, budget_s=120.0, max_steps=96, threads=2)
+    assert r["steps"] == 96 and r["kind"] == "oracle" and r["cores"] == 2
+    assert r["value"] > 0 and "96 single-token decode steps" in r["sample"]
+    # a tiny budget stops after the first step, never before it
+    r = bench.cpu_baseline(w, ht, host, budget_s=0.0, max_steps=96, threads=1)
+    assert r["steps"] == 1
+
+
+def test_cpu_baseline_gates_the_workload_highway(monkeypatch):
+    """Each step gates that step's highway from the workload's decode stream
+    (G.highway(w, n, decode=True)[step]), as the GPU decode leg does."""
+    import oracle
+    from synth import generate as G
+    w = synth.ODD_Q2K
+    ht = G.hash_tables(w)
+    host = [G.layer_inputs(w, ht, l) for l in range(w.n_layers)]
+    seen = []
+    real = oracle.gate_and_add
+
+    def spy(h, *a, **k):
+        seen.append(np.array(h, copy=True))
+        return real(h, *a, **k)
+
+    monkeypatch.setattr(oracle, "gate_and_add", spy)
+    bench.cpu_baseline(w, ht, host, budget_s=120.0, max_steps=3, threads=1)
+    hw = G.highway(w, 3, decode=True)
+    for step in range(3):
+        np.testing.assert_array_equal(seen[step * w.n_layers], hw[step:step + 1])
+
+
+def test_cpu_baseline_prefill_sample():
+    from synth import generate as G
+    w = synth.ODD_E4M3
+    ht = G.hash_tables(w)
+    host = [G.layer_inputs(w, ht, l) for l in range(w.n_layers)]
+    r = bench.cpu_baseline_prefill(w, ht, host, sample_tokens=8, threads=2)
+    assert r["tokens"] == 8 and r["cores"] == 2 and r["kind"] == "oracle"
+    assert r["value"] > 0 and "first 8 of the" in r["sample"]
+
+
+def test_oracle_threads_respects_omp_cap(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert 1 <= bench.oracle_threads() <= 3
