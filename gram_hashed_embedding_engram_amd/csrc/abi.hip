@@ -648,6 +648,8 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
     // and the last layer's gate moves it on
     const DecodePos dpos{ctx->step_start, ctx->graph_mode ? ctx->d_pos : nullptr, cfg.max_seq};
     int64_t *advance = ctx->graph_mode && hash_index == ctx->nl - 1 ? ctx->d_pos : nullptr;
+    // graph mode: a step refused on the device (past max_seq) gates nothing
+    const int32_t *refused = ctx->graph_mode ? ctx->err : nullptr;
     // one decode token of one sequence: hash, gather and projection in one launch
     if (one_launch) {
         rc = staged(ctx, 2, s, [&](const Launch &l) {
@@ -661,7 +663,7 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
             open_step(ctx, 1);
         return staged(ctx, 3, s, [&](const Launch &l) {
             return launch_gate(d_h, ctx->kv, L.qk, 1, cfg.hc, cfg.dim, cfg.eps, l, advance,
-                               cfg.max_seq);
+                               cfg.max_seq, refused);
         });
     }
     // one decode token of each of 2..4 sequences: the same, all tokens in one
@@ -679,7 +681,7 @@ int32_t engram_forward(engram_ctx *ctx, int32_t hash_index, const int32_t *d_ids
             open_step(ctx, 1);
         return staged(ctx, 3, s, [&](const Launch &l) {
             return launch_gate(d_h, ctx->kv, L.qk, M, cfg.hc, cfg.dim, cfg.eps, l, advance,
-                               cfg.max_seq);
+                               cfg.max_seq, refused);
         });
     }
     if (hash_index == 0) {

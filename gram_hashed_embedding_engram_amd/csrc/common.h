@@ -260,10 +260,12 @@ int32_t launch_dequant_q2k(const uint8_t *blocks, int64_t n_blocks, uint16_t *ou
 int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t K,
                     int64_t N, const Launch &l);
 // advance (nullable): a device position word that workgroup 0 moves one
-// step on, up to max_seq, after its row (the last layer of a replayed step)
+// step on, up to max_seq, after its row (the last layer of a replayed step);
+// err (nullable, graph mode): the device error word -- while it holds
+// ENGRAM_DEVERR_POSITION the gate leaves h untouched
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
                     int64_t dim, float eps, const Launch &l, int64_t *advance = nullptr,
-                    int64_t max_seq = 0);
+                    int64_t max_seq = 0, const int32_t *err = nullptr);
 int32_t launch_set_word(int64_t *p, int64_t v, const Launch &l);
 int32_t launch_qk_product(const uint16_t *q, const uint16_t *k, float *qk, int64_t n,
                           const Launch &l);

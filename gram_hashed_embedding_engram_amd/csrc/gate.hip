@@ -187,14 +187,24 @@ __device__ __forceinline__ void advance_step(int64_t *advance, int64_t max_seq)
     }
 }
 
+// Graph mode: a replayed step past max_seq (the step's first decode kernel
+// set ENGRAM_DEVERR_POSITION in the error word, which an earlier launch
+// wrote and nothing in this one does) leaves the highway as it was.
+__device__ __forceinline__ bool step_refused(const int32_t *err)
+{
+    return err && (*err & ENGRAM_DEVERR_POSITION);
+}
+
 template <int MAXI>
 __global__ __launch_bounds__(256) void gate_kernel(float *__restrict__ h,
                                                    const uint16_t *__restrict__ kv,
                                                    const float *__restrict__ qk, int64_t T,
                                                    int hc, int64_t dim, float eps, float fdim,
                                                    float inv_sqrt_dim, int64_t *advance,
-                                                   int64_t max_seq)
+                                                   int64_t max_seq, const int32_t *err)
 {
+    if (step_refused(err))
+        return;
     const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
     const int c = (int)(row - t * hc);
@@ -210,8 +220,11 @@ __global__ __launch_bounds__(256) void gate_kernel_any(float *__restrict__ h,
                                                        const float *__restrict__ qk, int64_t T,
                                                        int hc, int64_t dim, float eps,
                                                        float fdim, float inv_sqrt_dim,
-                                                       int64_t *advance, int64_t max_seq)
+                                                       int64_t *advance, int64_t max_seq,
+                                                       const int32_t *err)
 {
+    if (step_refused(err))
+        return;
     const int64_t row = token_row(blockIdx.x, T, hc);
     const int64_t t = row / hc;
     const int c = (int)(row - t * hc);
@@ -246,7 +259,8 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *__restrict__ p
 }  // namespace
 
 int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, int32_t hc,
-                    int64_t dim, float eps, const Launch &l, int64_t *advance, int64_t max_seq)
+                    int64_t dim, float eps, const Launch &l, int64_t *advance, int64_t max_seq,
+                    const int32_t *err)
 {
     const int64_t rows = T * hc;
     if (rows == 0)
@@ -258,14 +272,14 @@ int32_t launch_gate(float *h, const uint16_t *kv, const float *qk, int64_t T, in
 #define ENGRAM_GATE_CASE(I_)                                                                   \
     case I_:                                                                                   \
         dispatch(gate_kernel<I_>, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps, \
-                 fdim, inv_sqrt_dim, advance, max_seq);                                       \
+                 fdim, inv_sqrt_dim, advance, max_seq, err);                                  \
         break;
     switch (maxi) {
         ENGRAM_GATE_CASE(1) ENGRAM_GATE_CASE(2) ENGRAM_GATE_CASE(3) ENGRAM_GATE_CASE(4)
         ENGRAM_GATE_CASE(5) ENGRAM_GATE_CASE(6) ENGRAM_GATE_CASE(7) ENGRAM_GATE_CASE(8)
     default:
         dispatch(gate_kernel_any, grid, block, l, true, true, h, kv, qk, T, (int)hc, dim, eps,
-                 fdim, inv_sqrt_dim, advance, max_seq);
+                 fdim, inv_sqrt_dim, advance, max_seq, err);
         break;
     }
 #undef ENGRAM_GATE_CASE

@@ -364,8 +364,11 @@ int32_t engram_ctx_timing(engram_ctx *ctx, double *ms_per_stage /*[4]*/,
  * successive steps.  The caller writes each step's token ids into the d_ids
  * buffer it captured (and its highway into d_h) before a replay.  The host
  * no longer checks the position: a step at max_seq or beyond sets
- * ENGRAM_DEVERR_POSITION, writes no history and leaves its outputs
- * unspecified.  Stage timing must be off (its events cannot be captured).
+ * ENGRAM_DEVERR_POSITION and writes no history; while that bit is set (until
+ * engram_reset or engram_ctx_set_position clears the error word) every gate
+ * of graph mode leaves its highway untouched, and the step's row ids, rows
+ * and kv are unspecified.  Stage timing must be off (its events cannot be
+ * captured).
  *   enable = 1: enqueues the store of the host's position into the device
  *   word on `stream` (nothing if already enabled).  enable = 0: synchronises
  *   `stream` and reads the device word back as the host's position

@@ -116,3 +116,32 @@ class Device:
         import oracle
         L = self.layers[layer]
         return oracle.gather(L["table"], L["scales"], ids, self.w.head_dim, self.w.scale_block)
+
+
+# the prefill GEMM's output tile: 256 tokens x 320 outputs
+GEMM_TILE_M = 256
+GEMM_TILE_N = 320
+
+
+def tile_strata(n, tile, rng, interior=1):
+    """Indices into [0, n) that meet every tile of `tile` consecutive indices:
+    each tile's first and last index and `interior` seeded indices inside it.
+    Sampling tokens this way (all outputs of each) and outputs this way (all
+    tokens of each) puts a compared row slice and a compared column slice in
+    every output tile of the projection, so a tile that is skipped, written
+    twice or written to the wrong place cannot hide between samples."""
+    out = []
+    for s in range(0, n, tile):
+        e = min(s + tile, n)
+        out += [s, e - 1]
+        out += list(rng.integers(s, e, size=interior))
+    return np.unique(np.asarray(out, dtype=np.int64))
+
+
+def assert_tiles_covered(tokens, cols, T, N):
+    """Every (256-token, 320-output) tile holds a sampled token and a sampled
+    output."""
+    tm = set((np.asarray(tokens) // GEMM_TILE_M).tolist())
+    tn = set((np.asarray(cols) // GEMM_TILE_N).tolist())
+    assert tm == set(range(-(-T // GEMM_TILE_M))), "a token tile has no sample"
+    assert tn == set(range(-(-N // GEMM_TILE_N))), "an output tile has no sample"

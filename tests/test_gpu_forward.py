@@ -16,7 +16,8 @@ import pytest
 import oracle
 import synth
 from synth import generate as G
-from _gpu_util import Device, log, relerr, widen, to_np_u16
+from _gpu_util import (Device, log, relerr, widen, to_np_u16, tile_strata, assert_tiles_covered,
+                       GEMM_TILE_M, GEMM_TILE_N)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +40,10 @@ def cuda(a):
 def check_call(dev, ctx, layer, ids_np, hasher_out, h_before, h_after, T, sample_tokens=None,
                sample_cols=None, label=""):
     """Compare one forward call's intermediates and output with the oracle
-    (T = all tokens of the call, batch * tokens per sequence)."""
+    (T = all tokens of the call, batch * tokens per sequence): every row id and
+    row bit for bit, kv on the sampled tokens (all outputs) and the sampled
+    outputs (all tokens), or on everything, and the highway of every token
+    against the oracle gate of the GPU's kv."""
     w = dev.w
     rid, rows, kv = ctx.views(T // ctx.batch)
     rid = rid.cpu().numpy()
@@ -56,9 +60,10 @@ def check_call(dev, ctx, layer, ids_np, hasher_out, h_before, h_after, T, sample
         want_c = oracle.linear_bf16(rows, dev.oracle_wkv(layer)[sample_cols])
         e_c = relerr(widen(kv[:, sample_cols]), widen(want_c))
         assert e_c <= 1e-2, f"{label} kv cols relerr {e_c:.2e}"
+    # the gate over every token (cheap on the host), fed the GPU's own kv
     L = dev.layers[layer]
-    want_h = oracle.gate_and_add(h_before[toks], kv[toks], L["q"], L["k"], w.eps)
-    e_h = relerr(h_after[toks], want_h)
+    want_h = oracle.gate_and_add(h_before, kv, L["q"], L["k"], w.eps)
+    e_h = relerr(h_after, want_h)
     assert e_h <= 2e-3, f"{label} highway relerr {e_h:.2e}"
     return e_kv, e_h, kv
 
@@ -232,8 +237,9 @@ def test_forward_prefill_workload(E):
     ctx = dev.context(max_tokens=T, max_seq=T)
     want_ids = dev.oracle_hasher(T).hash(ids, 0)
     rng = np.random.default_rng(1)
-    toks = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.integers(0, T, 11)]))
-    cols = np.unique(np.concatenate([[0, 255, 256, 20479], rng.integers(0, 20480, 12)]))
+    toks = tile_strata(T, GEMM_TILE_M, rng)
+    cols = tile_strata(w.N, GEMM_TILE_N, rng)
+    assert_tiles_covered(toks, cols, T, w.N)
     d_ids = cuda(ids.astype(np.int32))
     for layer in range(2):
         d_h = torch.from_numpy(h0).cuda()
@@ -268,9 +274,12 @@ def test_forward_split_workload(E):
             d_h = torch.from_numpy(h0).cuda()
             ctx.forward(layer, d_ids[a:b] if layer == 0 else None, T, d_h)
             if full_check:
-                toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 6)]))
+                toks = tile_strata(T, GEMM_TILE_M, rng)
+                cols = tile_strata(w.N, GEMM_TILE_N, rng) if T > 1 else None
+                if T > 1:
+                    assert_tiles_covered(toks, cols, T, w.N)
                 check_call(dev, ctx, layer, ids[a:b], single[a:b], h0, d_h.cpu().numpy(), T,
-                           toks, label=f"split call {ci} layer {layer}")
+                           toks, cols, label=f"split call {ci} layer {layer}")
             else:
                 rid = ctx.views(T)[0].cpu().numpy()
                 np.testing.assert_array_equal(rid, single[a:b])
@@ -292,8 +301,9 @@ def test_forward_gather_stress(E):
     ctx.check()
     want_ids = dev.oracle_hasher(T).hash(ids, 0)
     rng = np.random.default_rng(4)
-    toks = np.unique(np.concatenate([[0, T - 1, 8191, 8192], rng.integers(0, T, 8)]))
-    cols = np.unique(np.concatenate([[0, 20479], rng.integers(0, 20480, 6)]))
+    toks = tile_strata(T, GEMM_TILE_M, rng)
+    cols = tile_strata(w.N, GEMM_TILE_N, rng)
+    assert_tiles_covered(toks, cols, T, w.N)
     e_kv, e_h, _ = check_call(dev, ctx, 0, ids, want_ids, h0, d_h.cpu().numpy(), T, toks, cols,
                               label="gather stress")
     log(f"  kv {e_kv:.2e} highway {e_h:.2e}")
@@ -378,8 +388,9 @@ def test_host_tables_match_device_tables(E, name, B):
     """Tables in pinned host memory, read by the kernels across the host link
     (the atlascybernetics engram_v41 page, EngramRowReader: rows fetched from
     wherever the table lives): the prompt and every decode step, one launch or
-    staged, leave exactly what device-resident tables leave -- row ids, rows,
-    kv and highway, bit for bit."""
+    staged, are checked against the oracle (ids and rows bit for bit, kv and
+    highway within tolerance) and leave exactly what device-resident tables
+    leave -- row ids, rows, kv and highway, bit for bit."""
     w = synth.WORKLOADS[name]
     prompt, steps = 8, 12
     log(f"host vs device tables: {name}, B={B}")
@@ -393,16 +404,25 @@ def test_host_tables_match_device_tables(E, name, B):
         for fused in (True, False):
             ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps, batch=B)
             ctx.set_fused_decode(fused)
+            hashers = [dev.oracle_hasher(prompt + steps) for _ in range(B)]
             d_ids = cuda(ids.astype(np.int32))
             out = []
             for step in range(1 + steps):
                 T = prompt if step == 0 else 1
                 p0 = 0 if step == 0 else prompt + step - 1
                 h0 = hp if step == 0 else hs[step - 1][:, None]
+                want_ids = np.concatenate([hashers[b].hash(ids[b, p0:p0 + T], p0)
+                                           for b in range(B)])
                 for layer in range(w.n_layers):
                     d_h = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
                     ctx.forward(layer, d_ids[:, p0:p0 + T].contiguous() if layer == 0 else None,
                                 T, d_h)
+                    if host:
+                        # the host-table path against the oracle itself
+                        check_call(dev, ctx, layer, None, want_ids,
+                                   np.ascontiguousarray(h0).reshape(B * T, w.hc, w.dim),
+                                   d_h.cpu().numpy().reshape(B * T, w.hc, w.dim), B * T,
+                                   label=f"host tables fused={fused} step {step} layer {layer}")
                     rid, rows, kv = ctx.views(T)
                     out.append((rid.cpu().numpy(), to_np_u16(rows), to_np_u16(kv),
                                 d_h.cpu().numpy().view(np.uint32)))
@@ -495,14 +515,78 @@ def test_graph_replay_matches_eager(E, name, B):
             np.testing.assert_array_equal(hbuf[layer].cpu().numpy().view(np.uint32), wh[layer],
                                           err_msg=f"step {step} layer {layer} highway")
     ctx.check()
-    # one replay past max_seq: reported on the device, position held at max_seq
+    # one replay past max_seq: reported on the device, position held at
+    # max_seq, and no gate touches the highway
+    h_keep = [torch.full_like(hb, 0.75) for hb in hbuf]
+    for hb, hk in zip(hbuf, h_keep):
+        hb.copy_(hk)
     g.replay()
     with pytest.raises(E.EngramError) as ei:
         ctx.check()
     assert ei.value.code == E.E_DEVICE and "max_seq" in str(ei.value)
+    for layer, (hb, hk) in enumerate(zip(hbuf, h_keep)):
+        assert torch.equal(hb, hk), f"layer {layer}: a refused step gated the highway"
     ctx.set_graph_mode(False)
     assert ctx.position == prompt + steps
     del g
+
+
+@pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 1), (synth.ODD_E4M3.name, 1),
+                                    (synth.DECODE_WKVQ2K.name, 1), (synth.DECODE_Q2K.name, 3),
+                                    (synth.ODD_Q2K.name, 2), (synth.MAX_SLOTS_Q2K.name, 1)])
+def test_graph_replay_matches_oracle(E, name, B):
+    """Replayed decode steps against the oracle itself (atlascybernetics
+    "deepseek_v41_layer.rs", GraphMode): each layer's step is captured into a
+    hipGraph of its own in graph mode, and every replay of every layer is
+    checked like an eager call -- row ids and rows bit for bit against the
+    oracle hasher and gather, kv within 1e-2 of the oracle projection, the
+    highway within 2e-3 of the oracle gate of the GPU's kv."""
+    dev = Device(name)
+    w = dev.w
+    prompt, steps = 6, 10
+    log(f"graph replay vs oracle: {name}, B={B}")
+    ids = G.token_ids(w, B * (prompt + steps)).reshape(B, prompt + steps)
+    hp = G.highway(w, B * prompt).reshape(B * prompt, w.hc, w.dim)
+    hs = G.highway(w, B * steps).reshape(steps, B, 1, w.hc, w.dim)
+    hashers = [dev.oracle_hasher(prompt + steps) for _ in range(B)]
+    ctx = dev.context(max_tokens=prompt, max_seq=prompt + steps, batch=B)
+    d_ids = cuda(ids.astype(np.int32))
+    want_ids = np.concatenate([hashers[b].hash(ids[b, :prompt], 0) for b in range(B)])
+    for layer in range(w.n_layers):
+        d_h = torch.from_numpy(hp).cuda()
+        ctx.forward(layer, d_ids[:, :prompt].contiguous() if layer == 0 else None, prompt, d_h)
+        check_call(dev, ctx, layer, None, want_ids, hp, d_h.cpu().numpy(), B * prompt,
+                   label=f"prompt layer {layer}")
+    ctx.set_graph_mode(True)
+    tok = torch.zeros(B, 1, dtype=torch.int32, device="cuda")
+    hbuf = [torch.zeros(B, 1, w.hc, w.dim, dtype=torch.float32, device="cuda")
+            for _ in range(w.n_layers)]
+    torch.cuda.synchronize()
+    graphs = []
+    for layer in range(w.n_layers):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ctx.forward(layer, tok if layer == 0 else None, 1, hbuf[layer])
+        graphs.append(g)
+    worst = [0.0, 0.0]
+    for step in range(steps):
+        p = prompt + step
+        tok.copy_(d_ids[:, p:p + 1])
+        want_ids = np.concatenate([hashers[b].hash(ids[b, p:p + 1], p) for b in range(B)])
+        h0 = np.ascontiguousarray(hs[step]).reshape(B, w.hc, w.dim)
+        for layer in range(w.n_layers):
+            hbuf[layer].copy_(torch.from_numpy(h0).reshape(B, 1, w.hc, w.dim))
+            graphs[layer].replay()
+            torch.cuda.synchronize()
+            e_kv, e_h, _ = check_call(dev, ctx, layer, None, want_ids, h0,
+                                      hbuf[layer].cpu().numpy().reshape(B, w.hc, w.dim), B,
+                                      label=f"replay step {step} layer {layer}")
+            worst = [max(worst[0], e_kv), max(worst[1], e_h)]
+    ctx.check()
+    ctx.set_graph_mode(False)
+    assert ctx.position == prompt + steps
+    log(f"  worst kv relerr {worst[0]:.2e}, highway {worst[1]:.2e}")
+    del graphs
 
 
 @pytest.mark.parametrize("name,B,fused", [(synth.DECODE_Q2K.name, 1, True),

@@ -12,7 +12,8 @@ import pytest
 
 import synth
 from synth import generate as G
-from _gpu_util import Device, log, relerr, widen, to_np_u16
+from _gpu_util import (Device, log, relerr, widen, to_np_u16, tile_strata, assert_tiles_covered,
+                       GEMM_TILE_M, GEMM_TILE_N)
 
 pytestmark = pytest.mark.gpu
 
@@ -383,12 +384,15 @@ def test_project_short_k(E, M, K, N):
 
 @pytest.mark.parametrize("M", [32, 4096])
 def test_project_gemm_full_shape(E, decode, M):
+    """The prefill shape (and a 32-token call): sampled by strata so every
+    256 x 320 output tile has a compared token row (all 20480 outputs) and a
+    compared output column (all M tokens)."""
     rng = np.random.default_rng(7 + M)
     ids = rng.integers(0, decode.layers[1]["rows"], size=(M, 24))
     x = decode.oracle_rows(1, ids).reshape(M, -1)
-    rows = np.unique(np.concatenate([[0, M - 1, 255, 256, M // 2], rng.integers(0, M, 8)]))
-    rows = rows[rows < M]
-    cols = np.unique(np.concatenate([[0, 20479, 255, 256, 4095, 4096], rng.integers(0, 20480, 26)]))
+    rows = tile_strata(M, GEMM_TILE_M, rng)
+    cols = tile_strata(20480, GEMM_TILE_N, rng)
+    assert_tiles_covered(rows, cols, M, 20480)
     log(f"project gemm: M={M} K=6144 N=20480 (sampled rows {rows.size}, cols {cols.size})")
     check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
 
