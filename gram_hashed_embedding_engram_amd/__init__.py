@@ -20,6 +20,7 @@ FMT_Q2K, FMT_E4M3 = 0, 1
 Q2K_ROW_BYTES = 84
 STREAM_ROW_BYTES = 12288      # engram_stream_read's row (ENGRAM_STREAM_ROW_BYTES)
 STREAM_SINK_WORDS = 8192      # its sink (ENGRAM_STREAM_SINK_WORDS)
+STATIC_SCRATCH_BYTES = 32 << 20   # engram_layer_static's scratch (ENGRAM_STATIC_SCRATCH_BYTES)
 STAGES = ("hash", "gather", "project", "gate")
 
 # Every symbol include/engram.h declares.
@@ -33,7 +34,7 @@ EXPORTS = (
     "engram_check", "engram_position", "engram_ctx_buffers", "engram_ctx_set_fused_decode",
     "engram_ctx_set_timing",
     "engram_ctx_timing", "engram_ctx_destroy", "engram_map_host", "engram_stream_read",
-    "engram_ctx_set_graph_mode", "engram_ctx_set_position",
+    "engram_ctx_set_graph_mode", "engram_ctx_set_position", "engram_layer_static",
 )
 
 
@@ -66,7 +67,7 @@ class ConfigC(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 6           # ENGRAM_ABI_VERSION of include/engram.h this binding follows
+ABI_VERSION = 7           # ENGRAM_ABI_VERSION of include/engram.h this binding follows
 
 
 def lib():
@@ -107,6 +108,8 @@ def lib():
             "engram_stream_read": (i32, [p, i64, p, p]),
             "engram_ctx_set_graph_mode": (i32, [p, i32, p]),
             "engram_ctx_set_position": (i32, [p, i64, p]),
+            "engram_layer_static": (i32, [p, i32, p, p, p, i32, i64, ctypes.c_float, p, i64,
+                                          i64, p, i64, p, p, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -301,6 +304,27 @@ def gate_apply(d_h, d_kv, d_qk, eps, stream=None):
     _need(d_qk, "qk", 4 * hc * dim)
     _check(lib().engram_gate_apply(_ptr(d_h), _ptr(d_kv), _ptr(d_qk), T, hc, dim,
                                    float(eps), _stream(stream)))
+
+
+def layer_static(tables: HashTables, hash_index, table: Table, d_wkv, d_qk, eps, d_ids,
+                 start_pos, d_history, d_h, d_err=None, stream=None):
+    """One engram layer over d_ids [T] at start_pos with its row ids, rows
+    and kv in the library's static scratch (engram_layer_static: allocates
+    nothing).  d_history [max_seq] int64, d_h [T, hc, dim] f32 in place."""
+    T = int(d_ids.numel())
+    _, hc, dim = d_h.shape
+    K = tables.cols * table.c.head_dim
+    _need(d_ids, "ids", 4 * T)
+    _need(d_history, "history", 8 * int(d_history.numel()))
+    _need(d_wkv, "wkv", 2 * dim * (hc + 1) * K)
+    _need(d_qk, "qk", 4 * hc * dim)
+    _need(d_h, "h", 4 * T * hc * dim)
+    _need(d_err, "err", 4)
+    _check(lib().engram_layer_static(ctypes.byref(tables.c), int(hash_index),
+                                     ctypes.byref(table.c), _ptr(d_wkv), _ptr(d_qk), int(hc),
+                                     int(dim), float(eps), _ptr(d_ids), T, int(start_pos),
+                                     _ptr(d_history), int(d_history.numel()), _ptr(d_h),
+                                     _ptr(d_err), _stream(stream)))
 
 
 class Context:

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -220,6 +221,50 @@ int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t 
 }  // namespace engram
 
 using namespace engram;
+
+// ------------------------------------- scratch of the call that allocates nothing
+
+// engram_layer_static keeps its call's row ids, rows and kv here instead of
+// in caller memory: one array per device, resident from the library's load
+// until the process ends.  Every call on a device shares that device's copy
+// and leaves the last call's contents in it, so calls that overlap on one
+// device race.  Host code never passes this name to a kernel (on the host it
+// is a stand-in, not a device address): it passes the address that
+// hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) uint8_t scratch[ENGRAM_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];     // per device, looked up once
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device with that device current, then reused.
+int32_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ENGRAM_E_HIP, "engram layer_static: hipGetDevice: %s", hipGetErrorString(e));
+    }
+    CHECK(dev >= 0 && dev < kMaxDevices, ENGRAM_E_HIP, "engram layer_static: device %d", dev);
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(ENGRAM_E_HIP, "engram layer_static: hipGetSymbolAddress(scratch): %s",
+                        hipGetErrorString(e));
+        }
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return ENGRAM_OK;
+}
+
+}  // namespace
 
 // ------------------------------------------------------------ the context
 
@@ -473,6 +518,75 @@ int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, i
     if (rc != ENGRAM_OK)
         return rc;
     return launch_gate(d_h, d_kv, d_qk, T, hc, dim, eps, on(stream));
+}
+
+int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index,
+                            const engram_table *table, const uint16_t *d_wkv, const float *d_qk,
+                            int32_t hc, int64_t dim, float eps, const int32_t *d_ids, int64_t T,
+                            int64_t start_pos, int64_t *d_history, int64_t max_seq, float *d_h,
+                            int32_t *d_err, void *stream)
+{
+    HashConsts c;
+    int32_t rc = make_consts(tables, &c);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(hash_index >= 0 && hash_index < c.nl, ENGRAM_E_ARG,
+          "engram layer_static: hash index %d outside 0..%d", hash_index, c.nl - 1);
+    rc = check_table(table);
+    if (rc != ENGRAM_OK)
+        return rc;
+    CHECK(T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
+          "engram layer_static: T %lld, start_pos %lld, max_seq %lld", (long long)T,
+          (long long)start_pos, (long long)max_seq);
+    CHECK(start_pos + T <= max_seq, ENGRAM_E_RANGE, "engram hasher: %lld positions, %lld needed",
+          (long long)max_seq, (long long)(start_pos + T));
+    int64_t need_rows = 0;
+    for (int col = 0; col < c.cols; col++) {
+        const int slot = hash_index * c.cols + col;
+        const int64_t top = c.offset[slot] + c.prime[slot];
+        need_rows = top > need_rows ? top : need_rows;
+    }
+    CHECK(table->n_rows >= need_rows, ENGRAM_E_RANGE,
+          "engram layer_static: table has %lld rows, the hash reaches row %lld",
+          (long long)table->n_rows, (long long)need_rows - 1);
+    const int64_t K = (int64_t)c.cols * table->head_dim, N = dim * (hc + 1);
+    // sizes (and, for T > 0, pointers) of the projection and the gate; rows
+    // and kv live in the 256-byte aligned scratch, so the caller's wkv stands
+    // in for them in the pointer checks
+    rc = check_gate(d_h, d_wkv, d_qk, T, hc, dim, eps);
+    if (rc != ENGRAM_OK)
+        return rc;
+    rc = check_project(d_wkv, d_wkv, d_wkv, T, K, N);
+    if (rc != ENGRAM_OK)
+        return rc;
+    const size_t off_rows = round256(sizeof(int64_t) * (size_t)(T * c.nl * c.cols));
+    const size_t off_kv = off_rows + round256(2 * (size_t)(T * K));
+    const size_t need = off_kv + round256(2 * (size_t)(T * N));
+    CHECK(need <= (size_t)ENGRAM_STATIC_SCRATCH_BYTES, ENGRAM_E_RANGE,
+          "engram layer_static: %lld tokens need %zu bytes of row ids, rows and kv; the static "
+          "scratch holds %lld",
+          (long long)T, need, (long long)ENGRAM_STATIC_SCRATCH_BYTES);
+    if (T == 0)
+        return ENGRAM_OK;
+    CHECK(d_ids && d_history, ENGRAM_E_ARG, "engram layer_static: NULL ids or history");
+    void *base = nullptr;
+    rc = scratch_address(&base);
+    if (rc != ENGRAM_OK)
+        return rc;
+    int64_t *row_ids = (int64_t *)base;
+    uint16_t *rows = (uint16_t *)((char *)base + off_rows);
+    uint16_t *kv = (uint16_t *)((char *)base + off_kv);
+    const Launch l = on(stream);
+    rc = launch_hash(c, tables->d_token_map, d_ids, 1, T, start_pos, d_history, max_seq, row_ids,
+                     d_err, l);
+    if (rc == ENGRAM_OK)
+        rc = launch_gather(*table, row_ids + (int64_t)hash_index * c.cols, T, c.cols,
+                           (int64_t)c.nl * c.cols, rows, d_err, l);
+    if (rc == ENGRAM_OK)
+        rc = dispatch_project(rows, d_wkv, kv, T, K, N, l);
+    if (rc == ENGRAM_OK)
+        rc = launch_gate(d_h, kv, d_qk, T, hc, dim, eps, l);
+    return rc;
 }
 
 size_t engram_workspace_bytes(const engram_config *cfg)

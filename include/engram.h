@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 6
+#define ENGRAM_ABI_VERSION 7
 
 #define ENGRAM_OK 0
 #define ENGRAM_E_ARG (-1)          /* null pointer, bad size or geometry          */
@@ -236,6 +236,34 @@ int32_t engram_qk_product(const uint16_t *d_q, const uint16_t *d_k, float *d_qk,
  *   dim a multiple of 256. */
 int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, int64_t T,
                           int32_t hc, int64_t dim, float eps, void *stream);
+
+/* ------------------------------------------- one layer, no caller scratch */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  One engram
+ * layer over T tokens of one sequence, computing what engram_forward
+ * computes for layer hash_index of a step at start_pos, with no context and
+ * no workspace: the step's row ids, rows and kv live in a static device array
+ * of ENGRAM_STATIC_SCRATCH_BYTES inside this library (one per device, held
+ * until the process ends), and the call allocates nothing.  The caller
+ * passes the inputs (hash tables, the layer's table, wkv [dim*(hc+1)]
+ * [cols*head_dim] bf16, qk [hc][dim] f32, ids [T] int32), the sequence's
+ * history [max_seq] int64 (read before start_pos, written at start_pos ..
+ * start_pos+T-1, as engram_hash does) and the highway h [T][hc][dim] f32,
+ * gated in place.  d_err nullable, as for engram_hash / engram_gather_dequant.
+ *   The scratch must hold T*n_layers*cols*8 + T*cols*head_dim*2 +
+ *   T*dim*(hc+1)*2 bytes (each part rounded up to 256): ENGRAM_E_RANGE
+ *   otherwise (at 2 layers of 24 columns, head_dim 256, dim 4096, hc 4: up to
+ *   625 tokens).
+ *   Every call on a device shares that device's scratch and leaves its
+ *   contents there: calls that overlap on one device (another stream,
+ *   another thread) race.  Checks as engram_forward's; T = 0 is a no-op. */
+#define ENGRAM_STATIC_SCRATCH_BYTES (32 << 20)
+int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index,
+                            const engram_table *table, const uint16_t *d_wkv, const float *d_qk,
+                            int32_t hc, int64_t dim, float eps, const int32_t *d_ids, int64_t T,
+                            int64_t start_pos, int64_t *d_history, int64_t max_seq, float *d_h,
+                            int32_t *d_err, void *stream);
 
 /* --------------------------------------------------- stateful engram layer */
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert sorted(E.EXPORTS) == names
-    assert L.engram_abi_version() == 6 == E.ABI_VERSION
+    assert L.engram_abi_version() == 7 == E.ABI_VERSION
     assert "#define ENGRAM_ABI_VERSION %d" % E.ABI_VERSION in open(HEADER).read()
 
 
@@ -352,3 +352,36 @@ def test_binding_refuses_short_buffers(monkeypatch):
             what="row_ids: the call needs 288 bytes, its storage holds 224")
     with pytest.raises(AssertionError, match="library was reached"):
         E.gather_dequant(table, ids2[:, 4:], 5, 4, 8, i16(5, 4 * 256), stream=0)
+
+
+def test_layer_static_refusals(L):
+    """The entry point that allocates nothing refuses, before any runtime
+    call, sizes its static scratch cannot hold and the arguments
+    engram_forward refuses."""
+    c, keep = tables_c()
+    # 2 layers x 101-row primes at offsets up to 47*101: 4848 rows needed
+    tab = E.TableC(E.FMT_Q2K, 256, 0, 0, 5000, FAKE, None)
+    sc = E.STATIC_SCRATCH_BYTES
+    assert "#define ENGRAM_STATIC_SCRATCH_BYTES (32 << 20)" in open(HEADER).read()
+    assert sc == 32 << 20
+
+    def call(T=4, layer=0, start=0, max_seq=4096, table=tab, hc=4, dim=4096, ids=FAKE,
+             wkv=FAKE, h=FAKE):
+        return rc_msg(L.engram_layer_static(ctypes.byref(c), layer, ctypes.byref(table), wkv,
+                                            FAKE, hc, dim, 1e-6, ids, T, start, FAKE, max_seq,
+                                            h, None, None))
+
+    # K = 24*256, N = 4096*5: 626 tokens need more than the 32 MiB scratch
+    rc, msg = call(T=626)
+    assert rc == E.E_RANGE and "scratch" in msg
+    assert call(layer=2)[0] == E.E_ARG
+    rc, msg = call(T=10, start=4090)
+    assert rc == E.E_RANGE and "4096 positions" in msg
+    small = E.TableC(E.FMT_Q2K, 256, 0, 0, 100, FAKE, None)
+    rc, msg = call(table=small)
+    assert rc == E.E_RANGE and "rows" in msg
+    assert call(hc=5)[0] == E.E_UNSUPPORTED
+    assert call(ids=None)[0] == E.E_ARG
+    assert call(wkv=None)[0] == E.E_ARG
+    assert call(h=FAKE + 4)[0] == E.E_ARG
+    assert call(T=0, ids=None, h=None)[0] == E.OK
