@@ -94,6 +94,25 @@ def counter_traffic(summary, kernel_src):
     return float(t.group(1))
 
 
+# VALU issue peak: 1024 SIMDs, one wave64 vector instruction every 4 cycles a
+# SIMD (16 lanes a cycle), 2.4 GHz
+VALU_PEAK_WAVE_INSTR = 1024 * 2.4e9 / 4
+
+
+def counter_value(summary, kernel_src, key):
+    """A per-launch figure (key: value) from a committed counter summary, if
+    it was taken on the current source of the kernel."""
+    path = os.path.join(PROFILE_DIR, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(key + r":\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest(kernel_src):
+        return None
+    return float(t.group(1))
+
+
 def device_inputs(w, torch, E, G):
     ht = G.hash_tables(w)
     tm = torch.from_numpy(ht["token_map"]).cuda()
@@ -680,6 +699,20 @@ def cpu_baseline_prefill(w, ht, host, sample_tokens=64, threads=None):
                        f"layer (hash, gather + dequant, projection, gate), {el:.1f} s")
 
 
+def q2kw_valu_roofline(avg_ms, w):
+    """The Q2_K-wkv decode kernel against the vector-ALU issue peak: its
+    wave64 VALU instructions per launch (committed counter summary, current
+    source only) over the live average launch time."""
+    instr = counter_value("decode_q2kw_counters.md", "decode.hip", "valu_instructions_per_launch")
+    if instr is None:
+        return None
+    achieved = instr / (avg_ms / 1e3)
+    return {"bound": "alu", "achieved": achieved / 1e9, "peak": VALU_PEAK_WAVE_INSTR / 1e9,
+            "unit": "G wave64 VALU instructions/s", "frac": achieved / VALU_PEAK_WAVE_INSTR,
+            "instructions_per_launch": instr,
+            "lane_instructions_per_weight": instr * 64 / (w.N * w.K)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -854,6 +887,7 @@ def main():
             "traffic": counter_traffic("decode_q2kw_counters.md", "decode.hip"),
             "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
             "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
+            "roofline": q2kw_valu_roofline(decq["proj_avg_ms"], wq),
             "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
                        "stages_ms_per_layer_step": decq_staged["stages"]}},
         "decode_graph": graph,

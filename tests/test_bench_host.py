@@ -108,3 +108,22 @@ def test_cpu_baseline_prefill_sample():
 def test_oracle_threads_respects_omp_cap(monkeypatch):
     monkeypatch.setenv("OMP_NUM_THREADS", "3")
     assert 1 <= bench.oracle_threads() <= 3
+
+
+def test_q2kw_valu_roofline_needs_the_current_digest(tmp_path, monkeypatch):
+    """The Q2_K-wkv decode kernel's VALU roofline: instructions per launch
+    from a counter summary taken on the current source, over the live launch
+    time, against 1024 SIMDs x 2.4 GHz / 4 cycles a wave64 instruction."""
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    w = synth.DECODE_WKVQ2K
+    (tmp_path / "decode_q2kw_counters.md").write_text(
+        f"source_sha256_16: {bench.source_digest('decode.hip')}\n"
+        "valu_instructions_per_launch: 9830400\nhbm_bytes_per_launch: 1\n")
+    r = bench.q2kw_valu_roofline(0.02, w)
+    assert r["bound"] == "alu" and abs(r["peak"] - 614.4) < 1e-9
+    assert abs(r["achieved"] - 9830400 / 0.02e-3 / 1e9) < 1e-6
+    assert abs(r["frac"] - 9830400 / 0.02e-3 / (1024 * 2.4e9 / 4)) < 1e-12
+    assert abs(r["lane_instructions_per_weight"] - 9830400 * 64 / (20480 * 6144)) < 1e-12
+    (tmp_path / "decode_q2kw_counters.md").write_text(
+        "source_sha256_16: 0000000000000000\nvalu_instructions_per_launch: 9830400\n")
+    assert bench.q2kw_valu_roofline(0.02, w) is None
