@@ -577,13 +577,20 @@ int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index
     uint16_t *rows = (uint16_t *)((char *)base + off_rows);
     uint16_t *kv = (uint16_t *)((char *)base + off_kv);
     const Launch l = on(stream);
-    rc = launch_hash(c, tables->d_token_map, d_ids, 1, T, start_pos, d_history, max_seq, row_ids,
-                     d_err, l);
-    if (rc == ENGRAM_OK)
-        rc = launch_gather(*table, row_ids + (int64_t)hash_index * c.cols, T, c.cols,
-                           (int64_t)c.nl * c.cols, rows, d_err, l);
-    if (rc == ENGRAM_OK)
-        rc = dispatch_project(rows, d_wkv, kv, T, K, N, l);
+    if (T == 1 && table->head_dim == 256 && c.cols <= kDecodeMaxCols) {
+        // one decode token: hash, gather + dequant and projection in one launch
+        const DecodePos dpos{start_pos, nullptr, max_seq};
+        rc = launch_decode(c, tables->d_token_map, d_ids, dpos, d_history, hash_index, true,
+                           *table, d_wkv, nullptr, kv, N, row_ids, rows, d_err, l);
+    } else {
+        rc = launch_hash(c, tables->d_token_map, d_ids, 1, T, start_pos, d_history, max_seq,
+                         row_ids, d_err, l);
+        if (rc == ENGRAM_OK)
+            rc = launch_gather(*table, row_ids + (int64_t)hash_index * c.cols, T, c.cols,
+                               (int64_t)c.nl * c.cols, rows, d_err, l);
+        if (rc == ENGRAM_OK)
+            rc = dispatch_project(rows, d_wkv, kv, T, K, N, l);
+    }
     if (rc == ENGRAM_OK)
         rc = launch_gate(d_h, kv, d_qk, T, hc, dim, eps, l);
     return rc;

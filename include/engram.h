@@ -257,7 +257,10 @@ int32_t engram_gate_apply(float *d_h, const uint16_t *d_kv, const float *d_qk, i
  *   625 tokens).
  *   Every call on a device shares that device's scratch and leaves its
  *   contents there: calls that overlap on one device (another stream,
- *   another thread) race.  Checks as engram_forward's; T = 0 is a no-op. */
+ *   another thread) race.  One token (head_dim 256, at most 32 columns) runs
+ *   hash, gather and projection as one kernel, then the gate, as
+ *   engram_forward's decode step does; more tokens run the staged kernels.
+ *   Checks as engram_forward's; T = 0 is a no-op. */
 #define ENGRAM_STATIC_SCRATCH_BYTES (32 << 20)
 int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index,
                             const engram_table *table, const uint16_t *d_wkv, const float *d_qk,
