@@ -397,6 +397,21 @@ def test_project_gemm_full_shape(E, decode, M):
     check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
 
 
+@pytest.mark.parametrize("M", [300, 1000, 4133])
+def test_project_gemm_ragged_full_k(E, decode, M):
+    """Token counts that leave a partly filled last 256-token tile, at the
+    decode workload's K and N (6144, 20480), sampled by tile strata against
+    the oracle: the tail rows read as zeros past M and are never stored."""
+    rng = np.random.default_rng(17 + M)
+    ids = rng.integers(0, decode.layers[0]["rows"], size=(M, 24))
+    x = decode.oracle_rows(0, ids).reshape(M, -1)
+    rows = tile_strata(M, GEMM_TILE_M, rng)
+    cols = tile_strata(20480, GEMM_TILE_N, rng)
+    assert_tiles_covered(rows, cols, M, 20480)
+    log(f"project gemm ragged: M={M} K=6144 N=20480 (sampled rows {rows.size}, cols {cols.size})")
+    check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"], rows, cols)
+
+
 def test_project_run_twice_bit_identical(E, decode):
     """Every projection kernel is deterministic: the same call twice gives
     the same bits, at the token counts that select each kernel (one-token
