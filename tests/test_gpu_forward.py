@@ -125,7 +125,9 @@ def test_forward_decode_workload(E):
 
 @pytest.mark.parametrize("name", [synth.ODD_Q2K.name, synth.ODD_E4M3.name,
                                   synth.ODD_WKVQ2K.name, synth.ODD_E4M3_WKVQ2K.name,
-                                  synth.MAX_SLOTS_Q2K.name, synth.MAX_NGRAM_E4M3.name])
+                                  synth.MAX_SLOTS_Q2K.name, synth.MAX_NGRAM_E4M3.name,
+                                  synth.HC1_Q2K.name, synth.HC3_E4M3.name,
+                                  synth.HC2_WKVQ2K.name])
 def test_forward_edge_geometry(E, name):
     """Edge-case hash geometries: an odd number of columns (5: K 1280, an
     odd number of 1 KiB loads a row, a partial last sub-block round), the
@@ -356,7 +358,8 @@ def run_steps(dev, ctx, ids, steps, prompt, h_prompt, h_steps):
                                   synth.DECODE_WKVQ2K.name, synth.ODD_Q2K.name,
                                   synth.ODD_E4M3.name, synth.ODD_WKVQ2K.name,
                                   synth.ODD_E4M3_WKVQ2K.name, synth.MAX_SLOTS_Q2K.name,
-                                  synth.MAX_NGRAM_E4M3.name])
+                                  synth.MAX_NGRAM_E4M3.name, synth.HC1_Q2K.name,
+                                  synth.HC3_E4M3.name, synth.HC2_WKVQ2K.name])
 def test_fused_decode_matches_staged(E, name):
     """The one-launch decode layer (hash + gather + projection) leaves exactly
     what the staged kernels leave: row ids, rows, kv and highway, bit for bit."""
@@ -533,7 +536,8 @@ def test_graph_replay_matches_eager(E, name, B):
 
 @pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 1), (synth.ODD_E4M3.name, 1),
                                     (synth.DECODE_WKVQ2K.name, 1), (synth.DECODE_Q2K.name, 3),
-                                    (synth.ODD_Q2K.name, 2), (synth.MAX_SLOTS_Q2K.name, 1)])
+                                    (synth.ODD_Q2K.name, 2), (synth.MAX_SLOTS_Q2K.name, 1),
+                                    (synth.HC1_Q2K.name, 1), (synth.HC3_E4M3.name, 3)])
 def test_graph_replay_matches_oracle(E, name, B):
     """Replayed decode steps against the oracle itself (atlascybernetics
     "deepseek_v41_layer.rs", GraphMode): each layer's step is captured into a
@@ -652,7 +656,7 @@ def test_map_host_refuses_unpinned_memory(E):
 
 
 @pytest.mark.parametrize("name", [synth.DECODE_WKVQ2K.name, synth.ODD_WKVQ2K.name,
-                                  synth.ODD_E4M3_WKVQ2K.name])
+                                  synth.ODD_E4M3_WKVQ2K.name, synth.HC2_WKVQ2K.name])
 def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
     """Workloads with Q2_K wkv: every step through the kernels over the
     blocks (one launch or staged) leaves exactly what the bf16 kernels over
@@ -684,7 +688,8 @@ def test_wkv_q2k_forward_matches_bf16_expansion(E, name):
 @pytest.mark.parametrize("name,B", [(synth.DECODE_Q2K.name, 2), (synth.DECODE_Q2K.name, 3),
                                     (synth.DECODE_Q2K.name, 4), (synth.ODD_Q2K.name, 3),
                                     (synth.ODD_E4M3.name, 4), (synth.MAX_SLOTS_Q2K.name, 3),
-                                    (synth.MAX_NGRAM_E4M3.name, 2)])
+                                    (synth.MAX_NGRAM_E4M3.name, 2), (synth.HC1_Q2K.name, 4),
+                                    (synth.HC3_E4M3.name, 3)])
 def test_fused_batched_decode_matches_staged(E, name, B):
     """B sequences' decode steps through the one-launch several-sequence
     kernel leave exactly what the staged kernels leave (row ids, rows, kv,
