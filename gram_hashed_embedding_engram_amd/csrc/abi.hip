@@ -68,8 +68,16 @@ namespace {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Positions start_pos .. start_pos+T-1 lie inside a history of max_seq
+// entries (all three non-negative; written so that no sum can overflow).
+bool fits_history(int64_t start_pos, int64_t T, int64_t max_seq)
+{
+    return start_pos <= max_seq && T <= max_seq - start_pos;
+}
+
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
 constexpr int32_t kMaxBatch = 4096;         // sequences per context
+constexpr int64_t kMaxSeq = (int64_t)1 << 40; // history entries per context
 
 // Hash tables -> kernel constants (atlascybernetics "engram_v41.rs",
 // EngramHashTables::from_flat: geometry and array checks).
@@ -151,7 +159,7 @@ int32_t check_project(const uint16_t *x, const uint16_t *w, const uint16_t *y, i
           "engram project: N = %lld must be a positive multiple of 16", (long long)N);
     // the GEMM addresses each operand with 32-bit byte offsets, tile tails
     // (up to 255 rows past the end) included
-    CHECK((T + 256) * K < kMaxElems && (N + 256) * K < kMaxElems && T * N < ((int64_t)1 << 40),
+    CHECK(T < kMaxElems / K - 256 && N < kMaxElems / K - 256 && T * N < ((int64_t)1 << 40),
           ENGRAM_E_UNSUPPORTED, "engram project: operands of %lld x %lld x %lld exceed 2^31 elements",
           (long long)T, (long long)K, (long long)N);
     if (T == 0)
@@ -317,9 +325,15 @@ int64_t batch_of(const engram_config *cfg) { return cfg->batch > 0 ? cfg->batch 
 
 bool carve(const engram_config *cfg, Carve *c)
 {
+    // every field bounded first, so that no size below wraps round
     if (!cfg || cfg->max_tokens <= 0 || cfg->max_seq <= 0 || cfg->dim <= 0 || cfg->hc <= 0 ||
         cfg->head_dim <= 0 || cfg->hash.n_layers <= 0 || cfg->hash.max_ngram < 2 ||
         cfg->hash.n_heads <= 0 || cfg->batch < 0 || cfg->batch > kMaxBatch)
+        return false;
+    if (cfg->max_tokens > kMaxElems || cfg->max_seq > kMaxSeq || cfg->dim > (1 << 20) ||
+        cfg->hc > 4 || cfg->head_dim > 1024 || cfg->hash.n_layers > ENGRAM_MAX_LAYERS ||
+        cfg->hash.max_ngram > ENGRAM_MAX_NGRAM || cfg->hash.n_heads > ENGRAM_MAX_SLOTS ||
+        batch_of(cfg) * cfg->max_tokens > kMaxElems || batch_of(cfg) * cfg->max_seq > kMaxSeq)
         return false;
     const int64_t cols = (int64_t)(cfg->hash.max_ngram - 1) * cfg->hash.n_heads;
     const int64_t B = batch_of(cfg), M = B * cfg->max_tokens;
@@ -421,8 +435,9 @@ int32_t engram_hash_batch(const engram_hash_tables *tables, const int32_t *d_ids
     CHECK(B >= 0 && T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
           "engram hash: B %lld, T %lld, start_pos %lld, max_seq %lld", (long long)B,
           (long long)T, (long long)start_pos, (long long)max_seq);
-    CHECK(start_pos + T <= max_seq, ENGRAM_E_RANGE, "engram hasher: %lld positions, %lld needed",
-          (long long)max_seq, (long long)(start_pos + T));
+    CHECK(fits_history(start_pos, T, max_seq), ENGRAM_E_RANGE,
+          "engram hasher: %lld positions, %lld tokens from position %lld", (long long)max_seq,
+          (long long)T, (long long)start_pos);
     CHECK(B == 0 || T == 0 || B <= ((int64_t)1 << 40) / T, ENGRAM_E_RANGE,
           "engram hash: %lld x %lld tokens", (long long)B, (long long)T);
     if (B == 0 || T == 0)
@@ -450,6 +465,8 @@ int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_id
     CHECK(T >= 0 && cols >= 1 && id_stride >= cols, ENGRAM_E_ARG,
           "engram gather: T %lld, cols %d, id_stride %lld", (long long)T, cols,
           (long long)id_stride);
+    CHECK(id_stride <= ENGRAM_MAX_SLOTS && T <= ((int64_t)1 << 40) / id_stride, ENGRAM_E_RANGE,
+          "engram gather: %lld tokens of %lld ids", (long long)T, (long long)id_stride);
     if (T == 0)
         return ENGRAM_OK;
     CHECK(d_row_ids && d_rows, ENGRAM_E_ARG, "engram gather: NULL pointer");
@@ -538,8 +555,9 @@ int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index
     CHECK(T >= 0 && start_pos >= 0 && max_seq >= 0, ENGRAM_E_ARG,
           "engram layer_static: T %lld, start_pos %lld, max_seq %lld", (long long)T,
           (long long)start_pos, (long long)max_seq);
-    CHECK(start_pos + T <= max_seq, ENGRAM_E_RANGE, "engram hasher: %lld positions, %lld needed",
-          (long long)max_seq, (long long)(start_pos + T));
+    CHECK(fits_history(start_pos, T, max_seq), ENGRAM_E_RANGE,
+          "engram hasher: %lld positions, %lld tokens from position %lld", (long long)max_seq,
+          (long long)T, (long long)start_pos);
     int64_t need_rows = 0;
     for (int col = 0; col < c.cols; col++) {
         const int slot = hash_index * c.cols + col;
@@ -624,14 +642,19 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
     CHECK(cfg->max_tokens >= 1 && cfg->max_seq >= 1, ENGRAM_E_ARG,
           "engram ctx: max_tokens %lld, max_seq %lld", (long long)cfg->max_tokens,
           (long long)cfg->max_seq);
+    CHECK(cfg->max_tokens <= kMaxElems && cfg->max_seq <= kMaxSeq &&
+              batch_of(cfg) * cfg->max_seq <= kMaxSeq && cfg->dim <= (1 << 20),
+          ENGRAM_E_UNSUPPORTED, "engram ctx: max_tokens %lld, max_seq %lld x %lld, dim %lld",
+          (long long)cfg->max_tokens, (long long)batch_of(cfg), (long long)cfg->max_seq,
+          (long long)cfg->dim);
     const int64_t K = (int64_t)c.cols * cfg->head_dim, N = cfg->dim * (cfg->hc + 1);
     CHECK(K % 64 == 0, ENGRAM_E_UNSUPPORTED, "engram ctx: cols*head_dim = %lld not a multiple of 64",
           (long long)K);
-    CHECK((batch_of(cfg) * cfg->max_tokens + 256) * K < kMaxElems && (N + 256) * K < kMaxElems,
+    CHECK(batch_of(cfg) * cfg->max_tokens < kMaxElems / K - 256 && N < kMaxElems / K - 256,
           ENGRAM_E_UNSUPPORTED,
           "engram ctx: projection operands exceed 2^31 elements");
     Carve cv;
-    carve(cfg, &cv);
+    CHECK(carve(cfg, &cv), ENGRAM_E_UNSUPPORTED, "engram ctx: geometry out of range");
     CHECK(d_workspace && aligned(d_workspace, 256), ENGRAM_E_ARG,
           "engram ctx: workspace must be non-NULL and 256-byte aligned");
     CHECK(workspace_bytes >= cv.total, ENGRAM_E_RANGE, "engram ctx: workspace %zu bytes, %zu needed",

@@ -280,10 +280,12 @@ int32_t engram_layer_static(const engram_hash_tables *tables, int32_t hash_index
  * pass over each layer's weights.  Calls on one context must not overlap. */
 typedef struct engram_ctx engram_ctx;
 
-/* Geometry: hc in 1..4; dim a multiple of 256; head_dim of every layer's
- * table; eps of the gate; batch sequences (0 or 1: one; up to 4096);
+/* Geometry: hc in 1..4; dim a multiple of 256 up to 2^20; head_dim of every
+ * layer's table; eps of the gate; batch sequences (0 or 1: one; up to 4096);
  * max_tokens per sequence per call; max_seq positions of history per
- * sequence.  hash.multipliers/primes/offsets are copied at create. */
+ * sequence (batch * max_seq at most 2^40; batch * max_tokens * cols *
+ * head_dim below 2^31, the projection's operand limit).
+ * hash.multipliers/primes/offsets are copied at create. */
 typedef struct engram_config {
     int32_t hc;
     int32_t head_dim;

@@ -61,7 +61,12 @@ def test_hash_refusals(L):
     call = lambda tab, T=4, start=0, max_seq=16: rc_msg(L.engram_hash(
         ctypes.byref(tab), FAKE, T, start, FAKE, max_seq, FAKE, None, None))
     rc, msg = call(c, T=10, start=8, max_seq=16)
-    assert rc == E.E_RANGE and "16 positions, 18 needed" in msg
+    assert rc == E.E_RANGE and "16 positions, 10 tokens from position 8" in msg
+    # positions near 2^63: refused without the sum start + T wrapping round
+    big = (1 << 62) + 1
+    assert call(c, T=big, start=big, max_seq=1 << 62)[0] == E.E_RANGE
+    assert call(c, T=2, start=(1 << 63) - 1, max_seq=(1 << 63) - 1)[0] == E.E_RANGE
+    assert call(c, T=(1 << 63) - 1, start=1, max_seq=(1 << 63) - 1)[0] == E.E_RANGE
     bad, k2 = tables_c(ng=1)
     assert call(bad)[0] == E.E_ARG
     bad, k3 = tables_c(ng=9, primes=np.full((2, 64), 101, np.int64),
@@ -139,6 +144,12 @@ def test_gather_refusals(L):
                                    None) == E.E_ARG
     # T = 0 is a no-op that launches nothing
     assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 0, 24, 48, FAKE, None, None) == E.OK
+    # row counts past 2^40 ids (T * cols would wrap round) and id strides
+    # wider than any hash geometry
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 1 << 60, 24, 48, FAKE, None,
+                                   None) == E.E_RANGE
+    assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 1 << 40, FAKE, None,
+                                   None) == E.E_RANGE
 
 
 def test_project_refusals(L):
@@ -148,6 +159,9 @@ def test_project_refusals(L):
     assert L.engram_project(None, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
     assert L.engram_project(FAKE + 8, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
     assert L.engram_project(FAKE, FAKE, FAKE, 1 << 20, 1 << 14, 64, None) == E.E_UNSUPPORTED
+    # token and output counts whose element counts would wrap round 2^63
+    assert L.engram_project(FAKE, FAKE, FAKE, (1 << 62) - 7, 64, 64, None) == E.E_UNSUPPORTED
+    assert L.engram_project(FAKE, FAKE, FAKE, 4, 64, (1 << 62) - 16, None) == E.E_UNSUPPORTED
     assert L.engram_project(FAKE, FAKE, FAKE, 0, 6144, 20480, None) == E.OK
 
 
@@ -206,6 +220,11 @@ def test_workspace_layout(L):
     for bad_batch in (-1, 4097):
         bad, _ = make_cfg(batch=bad_batch)
         assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0
+    # sizes whose byte counts would wrap round 2^64 are refused, not wrapped
+    for kw in ({"max_seq": 1 << 61}, {"max_tokens": 1 << 60}, {"dim": 1 << 40},
+               {"batch": 4096, "max_seq": 1 << 30}, {"batch": 4096, "max_tokens": 1 << 20}):
+        bad, _ = make_cfg(**kw)
+        assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0, kw
 
 
 def test_context_refusals_and_state(L):
@@ -220,6 +239,10 @@ def test_context_refusals_and_state(L):
     bad, k3 = make_cfg(dim=1000)
     assert L.engram_ctx_create(ctypes.byref(bad), FAKE, 1 << 40, ctypes.byref(h)) \
         == E.E_UNSUPPORTED
+    for kw in ({"max_seq": 1 << 61}, {"max_tokens": 1 << 60}, {"dim": 1 << 40}):
+        bad, _ = make_cfg(**kw)
+        assert L.engram_ctx_create(ctypes.byref(bad), FAKE, 1 << 62, ctypes.byref(h)) \
+            == E.E_UNSUPPORTED, kw
     assert L.engram_ctx_create(ctypes.byref(cfg), FAKE, n, ctypes.byref(h)) == E.OK
     try:
         assert L.engram_position(h) == 0
@@ -377,6 +400,7 @@ def test_layer_static_refusals(L):
     assert call(layer=2)[0] == E.E_ARG
     rc, msg = call(T=10, start=4090)
     assert rc == E.E_RANGE and "4096 positions" in msg
+    assert call(T=2, start=(1 << 63) - 1, max_seq=(1 << 63) - 1)[0] == E.E_RANGE
     small = E.TableC(E.FMT_Q2K, 256, 0, 0, 100, FAKE, None)
     rc, msg = call(table=small)
     assert rc == E.E_RANGE and "rows" in msg
