@@ -31,8 +31,9 @@ def cuda(a):
 
 
 @pytest.mark.parametrize("name,calls", [(synth.DECODE_Q2K.name, (32, 1, 1)),
-                                        (synth.TINY_E4M3.name, (64, 7)),
-                                        (synth.ODD_Q2K.name, (8, 3, 1))])
+                                        (synth.TINY_E4M3.name, (64, 7, 1)),
+                                        (synth.ODD_Q2K.name, (8, 3, 1)),
+                                        (synth.ODD_E4M3.name, (5, 1))])
 def test_layer_static_matches_forward(E, name, calls):
     import oracle
     dev = Device(name)
