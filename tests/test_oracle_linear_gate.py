@@ -73,6 +73,14 @@ def test_linear_equals_sequential_f32_sum(orc):
         for o in range(50):
             want[r, o] = np.cumsum(xf[r] * wf[o], dtype=np.float32)[-1]
     np.testing.assert_array_equal(orc.linear_bf16(x, w), bf16(want))
+    # where the order shows through the bf16 result: in f32, 2^24 + 1 is a tie
+    # that rounds back to 2^24 (even), while -2^24 + 1 is exact.  In index
+    # order 2^24 + 1 - 2^24 gives 0 and -2^24 + 1 + 2^24 gives 1; the reversed
+    # order swaps the two
+    ones = bf16(np.ones((1, 3)))
+    wc = bf16(np.array([[2.0 ** 24, 1.0, -(2.0 ** 24)], [-(2.0 ** 24), 1.0, 2.0 ** 24],
+                        [1.0, 2.0 ** 24, -(2.0 ** 24)]]))
+    np.testing.assert_array_equal(widen(orc.linear_bf16(ones, wc)), [[0.0, 1.0, 0.0]])
 
 
 def test_linear_threads_invariant(orc):
