@@ -159,7 +159,7 @@ def test_project_refusals(L):
     assert L.engram_project(None, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
     assert L.engram_project(FAKE + 8, FAKE, FAKE, 4, 6144, 20480, None) == E.E_ARG
     assert L.engram_project(FAKE, FAKE, FAKE, 1 << 20, 1 << 14, 64, None) == E.E_UNSUPPORTED
-    # token and output counts whose element counts would wrap round 2^63
+    # token and output counts whose element counts would overflow 2^63
     assert L.engram_project(FAKE, FAKE, FAKE, (1 << 62) - 7, 64, 64, None) == E.E_UNSUPPORTED
     assert L.engram_project(FAKE, FAKE, FAKE, 4, 64, (1 << 62) - 16, None) == E.E_UNSUPPORTED
     assert L.engram_project(FAKE, FAKE, FAKE, 0, 6144, 20480, None) == E.OK
@@ -220,7 +220,7 @@ def test_workspace_layout(L):
     for bad_batch in (-1, 4097):
         bad, _ = make_cfg(batch=bad_batch)
         assert L.engram_workspace_bytes(ctypes.byref(bad)) == 0
-    # sizes whose byte counts would wrap round 2^64 are refused, not wrapped
+    # sizes whose byte counts would overflow 2^64 are refused, not wrapped
     for kw in ({"max_seq": 1 << 61}, {"max_tokens": 1 << 60}, {"dim": 1 << 40},
                {"batch": 4096, "max_seq": 1 << 30}, {"batch": 4096, "max_tokens": 1 << 20}):
         bad, _ = make_cfg(**kw)
