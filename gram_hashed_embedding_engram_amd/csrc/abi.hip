@@ -325,7 +325,7 @@ int64_t batch_of(const engram_config *cfg) { return cfg->batch > 0 ? cfg->batch 
 
 bool carve(const engram_config *cfg, Carve *c)
 {
-    // every field bounded first, so that no size below wraps round
+    // every field bounded first, so that no size below overflows
     if (!cfg || cfg->max_tokens <= 0 || cfg->max_seq <= 0 || cfg->dim <= 0 || cfg->hc <= 0 ||
         cfg->head_dim <= 0 || cfg->hash.n_layers <= 0 || cfg->hash.max_ngram < 2 ||
         cfg->hash.n_heads <= 0 || cfg->batch < 0 || cfg->batch > kMaxBatch)

@@ -62,7 +62,7 @@ def test_hash_refusals(L):
         ctypes.byref(tab), FAKE, T, start, FAKE, max_seq, FAKE, None, None))
     rc, msg = call(c, T=10, start=8, max_seq=16)
     assert rc == E.E_RANGE and "16 positions, 10 tokens from position 8" in msg
-    # positions near 2^63: refused without the sum start + T wrapping round
+    # positions near 2^63: refused without the sum start + T overflowing
     big = (1 << 62) + 1
     assert call(c, T=big, start=big, max_seq=1 << 62)[0] == E.E_RANGE
     assert call(c, T=2, start=(1 << 63) - 1, max_seq=(1 << 63) - 1)[0] == E.E_RANGE
@@ -144,7 +144,7 @@ def test_gather_refusals(L):
                                    None) == E.E_ARG
     # T = 0 is a no-op that launches nothing
     assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 0, 24, 48, FAKE, None, None) == E.OK
-    # row counts past 2^40 ids (T * cols would wrap round) and id strides
+    # row counts past 2^40 ids (T * cols would overflow) and id strides
     # wider than any hash geometry
     assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 1 << 60, 24, 48, FAKE, None,
                                    None) == E.E_RANGE
