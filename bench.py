@@ -51,6 +51,23 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gram_hashed_embedding_engram_amd", "csrc")
 
 
+def run_leg(name, fn):
+    """One secondary leg of the run: its result, or -- if it raises -- an
+    error entry, so that one failing leg (or the CPU baseline) does not take
+    the measured ones and the line with them.  The traceback goes to stderr."""
+    import traceback
+    try:
+        return fn()
+    except Exception as e:           # the error is reported in the line and on stderr
+        traceback.print_exc()
+        log(f"{name}: failed: {type(e).__name__}: {e}")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def failed(r):
+    return isinstance(r, dict) and "error" in r
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -783,68 +800,98 @@ def main():
     inputs = device_inputs(synth.DECODE_Q2K, torch, E, G)
     dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=inputs)
     log(f"decode (fused): {dec['ms_per_step'] * 1e3:.1f} us/step, stages(ms) {dec['stages']}")
-    staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=inputs)
-    log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
-        f"{staged['stages']}")
+    staged = run_leg("decode (staged)", lambda: bench_decode(args, torch, E, G, synth,
+                                                             fused=False, inputs=inputs))
+    if not failed(staged):
+        log(f"decode (staged): {staged['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
+            f"{staged['stages']}")
     host_dec = None
     if args.host_tables:
-        hinputs = host_table_inputs(synth.DECODE_Q2K, inputs, torch, E)
-        host_dec = bench_decode(args, torch, E, G, synth, fused=True, inputs=hinputs)
-        log(f"decode (host tables): {host_dec['ms_per_step'] * 1e3:.1f} us/step, "
-            f"stages(ms) {host_dec['stages']}")
-        del hinputs
-    graph = bench_decode_graph(args, torch, E, G, synth, inputs)
-    log(f"decode (graph replay): {graph['ms_per_step'] * 1e3:.1f} us/step with the token copy, "
-        f"{graph['replay_only_ms_per_step'] * 1e3:.1f} us/step replay only; host "
-        f"{graph['host_ms_per_step'] * 1e3:.1f} / {graph['replay_only_host_ms_per_step'] * 1e3:.1f}"
-        f" us/step (eager {dec['host_ms_per_step'] * 1e3:.1f})")
+        def host_leg():
+            hinputs = host_table_inputs(synth.DECODE_Q2K, inputs, torch, E)
+            return bench_decode(args, torch, E, G, synth, fused=True, inputs=hinputs)
+        host_dec = run_leg("decode (host tables)", host_leg)
+        if not failed(host_dec):
+            log(f"decode (host tables): {host_dec['ms_per_step'] * 1e3:.1f} us/step, "
+                f"stages(ms) {host_dec['stages']}")
+    graph = run_leg("decode (graph replay)",
+                    lambda: bench_decode_graph(args, torch, E, G, synth, inputs))
+    if not failed(graph):
+        log(f"decode (graph replay): {graph['ms_per_step'] * 1e3:.1f} us/step with the token "
+            f"copy, {graph['replay_only_ms_per_step'] * 1e3:.1f} us/step replay only; host "
+            f"{graph['host_ms_per_step'] * 1e3:.1f} / "
+            f"{graph['replay_only_host_ms_per_step'] * 1e3:.1f} us/step (eager "
+            f"{dec['host_ms_per_step'] * 1e3:.1f})")
     batched = []
     for B in args.batch_sequences:
-        r = bench_decode_batched(args, torch, E, G, synth, inputs, B)
-        log(f"decode ({B} sequences): {r['ms_per_step'] * 1e3:.1f} us/step, "
-            f"{r['value']:.0f} tokens/s per layer, stages(ms) {r['stages_ms_per_layer_step']}")
+        r = run_leg(f"decode ({B} sequences)",
+                    lambda B=B: bench_decode_batched(args, torch, E, G, synth, inputs, B))
+        if not failed(r):
+            log(f"decode ({B} sequences): {r['ms_per_step'] * 1e3:.1f} us/step, "
+                f"{r['value']:.0f} tokens/s per layer, stages(ms) {r['stages_ms_per_layer_step']}")
         batched.append(r)
     wq = synth.DECODE_WKVQ2K
-    qinputs = wkv_q2k_inputs(wq, inputs, torch, E, G)
+
+    def q2kw_leg():
+        qinputs = wkv_q2k_inputs(wq, inputs, torch, E, G)
+        decq = bench_decode(args, torch, E, G, synth, fused=True, inputs=qinputs, w=wq)
+        log(f"decode (Q2_K wkv): {decq['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
+            f"{decq['stages']}")
+        decq_staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=qinputs, w=wq)
+        log(f"decode (Q2_K wkv, staged): {decq_staged['ms_per_step'] * 1e3:.1f} us/step, "
+            f"stages(ms) {decq_staged['stages']}")
+        return {
+            "workload": wq.name, "ms_per_step": decq["ms_per_step"], "value": decq["value"],
+            "unit": "engram tokens/s per layer",
+            "stages_ms_per_layer_step": decq["stages"],
+            "kernel": "decode_q2kw_kernel<Q2K,6> (hash + gather/dequant + projection off the "
+                      "Q2_K wkv blocks; vector-ALU bound)",
+            "bytes_per_launch": decq["proj_bytes"], "avg_launch_ms": decq["proj_avg_ms"],
+            "traffic": counter_traffic("decode_q2kw_counters.md", "decode.hip"),
+            "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
+            "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
+            "roofline": q2kw_valu_roofline(decq["proj_avg_ms"], wq),
+            "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
+                       "stages_ms_per_layer_step": decq_staged["stages"]}}
+    decode_wkv_q2k = run_leg("decode (Q2_K wkv)", q2kw_leg)
     del inputs
-    decq = bench_decode(args, torch, E, G, synth, fused=True, inputs=qinputs, w=wq)
-    log(f"decode (Q2_K wkv): {decq['ms_per_step'] * 1e3:.1f} us/step, stages(ms) "
-        f"{decq['stages']}")
-    decq_staged = bench_decode(args, torch, E, G, synth, fused=False, inputs=qinputs, w=wq)
-    log(f"decode (Q2_K wkv, staged): {decq_staged['ms_per_step'] * 1e3:.1f} us/step, "
-        f"stages(ms) {decq_staged['stages']}")
-    del qinputs
-    pre = None if args.no_prefill else bench_prefill(args, torch, E, G, synth)
-    if pre:
-        log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
-    stress = split = None
-    tiny = None if args.no_prefill else bench_tiny(args, torch, E, G, synth)
-    if tiny:
-        log(f"tiny: {tiny['ms_per_forward'] * 1e3:.1f} us a forward of {tiny['T']} tokens")
+    pre = None
     if not args.no_prefill:
-        stress = bench_gather_stress(args, torch, E, G, synth)
-        log(f"gather stress: {stress['ms_per_step']:.3f} ms/step, gather "
-            f"{stress['gather']['achieved']:.0f} GB/s, stages(ms) {stress['stages_ms']}")
-        split = bench_split(args, torch, E, G, synth)
-        log(f"split: prefill {split['prefill']['ms_per_chunk']:.3f} ms/chunk, decode "
-            f"{split['decode']['ms_per_step'] * 1e3:.1f} us/step")
+        pre = run_leg("prefill", lambda: bench_prefill(args, torch, E, G, synth))
+        if not failed(pre):
+            log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages(ms) {pre['stages_ms']}")
+    stress = split = tiny = None
+    if not args.no_prefill:
+        tiny = run_leg("tiny", lambda: bench_tiny(args, torch, E, G, synth))
+        if not failed(tiny):
+            log(f"tiny: {tiny['ms_per_forward'] * 1e3:.1f} us a forward of {tiny['T']} tokens")
+        stress = run_leg("gather stress", lambda: bench_gather_stress(args, torch, E, G, synth))
+        if not failed(stress):
+            log(f"gather stress: {stress['ms_per_step']:.3f} ms/step, gather "
+                f"{stress['gather']['achieved']:.0f} GB/s, stages(ms) {stress['stages_ms']}")
+        split = run_leg("split", lambda: bench_split(args, torch, E, G, synth))
+        if not failed(split):
+            log(f"split: prefill {split['prefill']['ms_per_chunk']:.3f} ms/chunk, decode "
+                f"{split['decode']['ms_per_step'] * 1e3:.1f} us/step")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
-        cpu = cpu_baseline(synth.DECODE_Q2K, dec["ht"], dec["host"], args.cpu_budget)
-        log(f"cpu baseline: {cpu['steps']} decode steps in {cpu['seconds']:.1f} s on "
-            f"{cpu['cores']} threads")
-        if pre:
-            pre["cpu_baseline"] = cpu_baseline_prefill(synth.PREFILL_Q2K, pre.pop("ht"),
-                                                       pre.pop("host"), args.cpu_prefill_tokens)
-            log(f"cpu baseline (prefill): {pre['cpu_baseline']['tokens']} tokens in "
-                f"{pre['cpu_baseline']['seconds']:.1f} s")
-    if pre:
+        cpu = run_leg("cpu baseline", lambda: cpu_baseline(synth.DECODE_Q2K, dec["ht"],
+                                                           dec["host"], args.cpu_budget))
+        if not failed(cpu):
+            log(f"cpu baseline: {cpu['steps']} decode steps in {cpu['seconds']:.1f} s on "
+                f"{cpu['cores']} threads")
+        if pre and not failed(pre):
+            pre["cpu_baseline"] = run_leg("cpu baseline (prefill)", lambda: cpu_baseline_prefill(
+                synth.PREFILL_Q2K, pre["ht"], pre["host"], args.cpu_prefill_tokens))
+            if not failed(pre["cpu_baseline"]):
+                log(f"cpu baseline (prefill): {pre['cpu_baseline']['tokens']} tokens in "
+                    f"{pre['cpu_baseline']['seconds']:.1f} s")
+    if pre and not failed(pre):
         pre.pop("ht", None)
         pre.pop("host", None)
     w = synth.DECODE_Q2K
     gbps = dec["proj_bytes"] / (dec["proj_avg_ms"] / 1e3) / 1e9
-    staged_gbps = staged["proj_bytes"] / (staged["proj_avg_ms"] / 1e3) / 1e9
     out = {
         "metric": "engram tokens/s per layer (decode T=1, prefill T=4096) + % HBM/MFMA roofline",
         "value_is": "decode T=1 on the decode workload (prefill T=4096: the prefill entry)",
@@ -872,26 +919,15 @@ def main():
         "hbm_read_ceiling": ceiling,
         "stages_ms_per_layer_step": dec["stages"],
         "host_ms_per_step": dec["host_ms_per_step"],
-        "decode_staged": {"ms_per_step": staged["ms_per_step"], "value": staged["value"],
-                          "stages_ms_per_layer_step": staged["stages"],
-                          "gemv_GBps": staged_gbps, "gather_GBps": staged["gather_GBps"],
-                          "gemv_traffic": counter_traffic("gemv_decode_counters.md",
-                                                          "gemv.hip")},
-        "decode_wkv_q2k": {
-            "workload": wq.name, "ms_per_step": decq["ms_per_step"], "value": decq["value"],
-            "unit": "engram tokens/s per layer",
-            "stages_ms_per_layer_step": decq["stages"],
-            "kernel": "decode_q2kw_kernel<Q2K,6> (hash + gather/dequant + projection off the "
-                      "Q2_K wkv blocks; vector-ALU bound)",
-            "bytes_per_launch": decq["proj_bytes"], "avg_launch_ms": decq["proj_avg_ms"],
-            "traffic": counter_traffic("decode_q2kw_counters.md", "decode.hip"),
-            "hbm_GBps": decq["proj_bytes"] / (decq["proj_avg_ms"] / 1e3) / 1e9,
-            "weights_per_s": wq.N * wq.K / (decq["proj_avg_ms"] / 1e3),
-            "roofline": q2kw_valu_roofline(decq["proj_avg_ms"], wq),
-            "staged": {"ms_per_step": decq_staged["ms_per_step"], "value": decq_staged["value"],
-                       "stages_ms_per_layer_step": decq_staged["stages"]}},
+        "decode_staged": staged if failed(staged) else {
+            "ms_per_step": staged["ms_per_step"], "value": staged["value"],
+            "stages_ms_per_layer_step": staged["stages"],
+            "gemv_GBps": staged["proj_bytes"] / (staged["proj_avg_ms"] / 1e3) / 1e9,
+            "gather_GBps": staged["gather_GBps"],
+            "gemv_traffic": counter_traffic("gemv_decode_counters.md", "gemv.hip")},
+        "decode_wkv_q2k": decode_wkv_q2k,
         "decode_graph": graph,
-        "decode_host_tables": None if host_dec is None else {
+        "decode_host_tables": host_dec if host_dec is None or failed(host_dec) else {
             "tables": "pinned host memory, rows read across the host link",
             "ms_per_step": host_dec["ms_per_step"], "value": host_dec["value"],
             "unit": "engram tokens/s per layer",

@@ -127,3 +127,17 @@ def test_q2kw_valu_roofline_needs_the_current_digest(tmp_path, monkeypatch):
     (tmp_path / "decode_q2kw_counters.md").write_text(
         "source_sha256_16: 0000000000000000\nvalu_instructions_per_launch: 9830400\n")
     assert bench.q2kw_valu_roofline(0.02, w) is None
+
+
+def test_run_leg_reports_a_failing_leg(capsys):
+    """A secondary leg that raises leaves an error entry (and its traceback
+    on stderr) instead of ending the run; a leg that works returns its result."""
+    assert bench.run_leg("ok", lambda: {"value": 1.0}) == {"value": 1.0}
+
+    def boom():
+        raise AssertionError("in_f")
+    r = bench.run_leg("cpu baseline", boom)
+    assert bench.failed(r) and r["error"] == "AssertionError: in_f"
+    err = capsys.readouterr().err
+    assert "cpu baseline: failed: AssertionError: in_f" in err and "Traceback" in err
+    assert not bench.failed({"value": 1.0}) and not bench.failed(None)
