@@ -335,6 +335,21 @@ def test_project_small_decode_shape(E, decode, M):
     check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 1024, 12320), (40, 1024, 12320), (24, 2048, 8208),
+                                   (64, 3072, 4112)])
+def test_project_few_token_ragged_rows(E, M, K, N):
+    """The few-token GEMM where its row tiles do not divide among the
+    workgroups (12320 outputs: 770 tiles of 16 in workgroups of 4, the last
+    one half empty; 8208: 513 tiles in threes) and where the rows fit one
+    workgroup a tile, with one to four token tiles (twelve and eight
+    wavefronts), against the oracle."""
+    rng = np.random.default_rng(M * 31 + N)
+    x = bf16_rand(rng, (M, K), 0.5)
+    w = bf16_rand(rng, (N, K), 0.05)
+    log(f"project few-token ragged: M={M} K={K} N={N}")
+    check_project(E, x, cuda(w), w)
+
+
 @pytest.mark.parametrize("T,K,N", [(2, 6144, 20480), (4, 6144, 20480), (3, 1280, 1008),
                                    (4, 8192, 2064), (2, 512, 16), (3, 1088, 4000)])
 def test_project_multi_token_equals_one_token(E, T, K, N):
