@@ -37,9 +37,9 @@ constexpr int kFewMaxRowTiles = 5;
 
 template <int RT, int MT, int W>
 __global__ __launch_bounds__(64 * W) void gemm_few_kernel(const uint16_t *__restrict__ A,
-                                                                  const uint16_t *__restrict__ B,
-                                                                  uint16_t *__restrict__ C, int M,
-                                                                  int N, int K)
+                                                          const uint16_t *__restrict__ B,
+                                                          uint16_t *__restrict__ C, int M, int N,
+                                                          int K)
 {
     constexpr int STAGE_B = W * RT * 16 * kFewRowBytes;
     constexpr int RED_B = W * RT * MT * 64 * 16;
