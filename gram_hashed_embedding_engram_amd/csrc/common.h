@@ -306,7 +306,7 @@ constexpr int64_t kQ2kWkvMaxK = 8192;
 
 // A few tokens (2..kGemmSmallMaxM) through the MFMA GEMM laid out as a weight
 // stream (gemm_small.hip); gemm_small_fits says whether the shape qualifies.
-constexpr int64_t kGemmSmallMaxM = 64;
+constexpr int64_t kGemmSmallMaxM = 128;
 bool gemm_small_fits(int64_t M, int64_t K, int64_t N);
 int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
                           int64_t K, int64_t N, const Launch &l);

@@ -1,9 +1,9 @@
-// Stage 3 for a few tokens (5..64): the wkv projection as a bf16 MFMA GEMM
+// Stage 3 for a few tokens (5..128): the wkv projection as a bf16 MFMA GEMM
 // with a short token dimension (atlascybernetics "spark_model/layers/
 // engram_v41.rs", module doc stage 3; metrale "deepseek_v41_ref/engram.rs",
 // linear_bf16) -- several sequences' decode tokens, short prompts.
 //
-// C[M][N] = A[M][K] * B[N][K]^T with A = the tokens (M <= 64), B = wkv.  At
+// C[M][N] = A[M][K] * B[N][K]^T with A = the tokens (M <= 128), B = wkv.  At
 // this M the GEMM is a single pass over wkv (252 MB at the decode shape), so
 // the kernel is laid out like a weight stream: a workgroup per CU owns 16*RT
 // consecutive output rows (RT <= 5) for all tokens and its wavefronts split
@@ -15,6 +15,11 @@
 // flight: with one (four a workgroup) it ran at about 4.9 TB/s, with three
 // at about 6.0.  So a workgroup has twelve wavefronts for one or two token
 // tiles and eight -- whose partial sums still fit in LDS -- for three or four.
+// Five to eight token tiles (65..128 tokens) take four wavefronts with 80
+// rows a workgroup: their accumulators need the AGPRs of a wavefront alone
+// on its SIMD, and every workgroup reads all the tokens, so fewer, wider
+// workgroups keep that traffic down (89 us at 128 tokens, against 166 us for
+// the tiled GEMM, whose 64 workgroups leave most CUs idle).
 #include "common.h"
 
 namespace engram {
@@ -157,9 +162,11 @@ int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int
     if (rt > kFewMaxRowTiles)
         rt = kFewMaxRowTiles;
     const int mt = (int)((M + 15) / 16);
+    if (mt > 4)
+        rt = kFewMaxRowTiles;     // five to eight token tiles: one shape, 80 rows a workgroup
     // twelve wavefronts for one or two token tiles, eight (whose partial sums
     // still fit in LDS) for three or four
-    const int waves = mt <= 2 ? 12 : 8;
+    const int waves = mt <= 2 ? 12 : mt <= 4 ? 8 : 4;
     const dim3 grid((unsigned)((tiles + rt - 1) / rt)), block(64 * waves);
 #define ENGRAM_FEW_CASE(R_, T_, W_)                                                              \
     if (rt == R_ && mt == T_) {                                                                  \
@@ -171,6 +178,8 @@ int32_t launch_gemm_small(const uint16_t *x, const uint16_t *w, uint16_t *y, int
     ENGRAM_FEW_CASE(R_, 1, 12) ENGRAM_FEW_CASE(R_, 2, 12) ENGRAM_FEW_CASE(R_, 3, 8)               \
     ENGRAM_FEW_CASE(R_, 4, 8)
     ENGRAM_FEW_ROW(1) ENGRAM_FEW_ROW(2) ENGRAM_FEW_ROW(3) ENGRAM_FEW_ROW(4) ENGRAM_FEW_ROW(5)
+    ENGRAM_FEW_CASE(5, 5, 4) ENGRAM_FEW_CASE(5, 6, 4) ENGRAM_FEW_CASE(5, 7, 4)
+    ENGRAM_FEW_CASE(5, 8, 4)
 #undef ENGRAM_FEW_ROW
 #undef ENGRAM_FEW_CASE
     return fail(ENGRAM_E_UNSUPPORTED, "engram small gemm: %lld tokens", (long long)M);

@@ -189,7 +189,7 @@ int32_t engram_gather_dequant(const engram_table *table, const int64_t *d_row_id
  * dim*(hc+1)]).  A bandwidth-bound GEMV serves T = 1 and 2 <= T <= 4 (the
  * tokens in one pass over the weights; each token's outputs then equal those
  * of a one-token call bit for bit), an MFMA GEMM laid out as a weight stream
- * 5 <= T <= 64 (K a multiple of 1024), the tiled MFMA GEMM larger T.
+ * 5 <= T <= 128 (K a multiple of 1024), the tiled MFMA GEMM larger T.
  *   d_x [T][K], d_w [N][K], d_y [T][N], all bf16; K a multiple of 64. */
 int32_t engram_project(const uint16_t *d_x, const uint16_t *d_w, uint16_t *d_y, int64_t T,
                        int64_t K, int64_t N, void *stream);

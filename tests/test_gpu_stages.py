@@ -322,12 +322,13 @@ def test_project_gemv_decode_shape(E, decode, T):
     check_project(E, x, decode.wkv[0], decode.layers[0]["wkv"])
 
 
-@pytest.mark.parametrize("M", [2, 5, 16, 17, 33, 64])
+@pytest.mark.parametrize("M", [2, 5, 16, 17, 33, 64, 65, 100, 128])
 def test_project_small_decode_shape(E, decode, M):
     """A few tokens (several sequences' decode tokens, short prompts) through
-    the decode-shape wkv: the multi-token GEMV (M <= 8) or the MFMA GEMM laid
-    out as a weight stream, every output checked (partial token tiles at
-    M = 17, 33)."""
+    the decode-shape wkv: the multi-token GEMV (M <= 4) or the MFMA GEMM laid
+    out as a weight stream (twelve, eight or four wavefronts a workgroup up to
+    128 tokens), every output checked (partial token tiles at M = 17, 33, 65,
+    100)."""
     rng = np.random.default_rng(100 + M)
     ids = rng.integers(0, decode.layers[0]["rows"], size=(M, 24))
     x = decode.oracle_rows(0, ids).reshape(M, -1)
@@ -336,13 +337,14 @@ def test_project_small_decode_shape(E, decode, M):
 
 
 @pytest.mark.parametrize("M,K,N", [(5, 1024, 12320), (40, 1024, 12320), (24, 2048, 8208),
-                                   (64, 3072, 4112)])
+                                   (64, 3072, 4112), (100, 1024, 12320), (128, 2048, 1296)])
 def test_project_few_token_ragged_rows(E, M, K, N):
     """The few-token GEMM where its row tiles do not divide among the
-    workgroups (12320 outputs: 770 tiles of 16 in workgroups of 4, the last
-    one half empty; 8208: 513 tiles in threes) and where the rows fit one
-    workgroup a tile, with one to four token tiles (twelve and eight
-    wavefronts), against the oracle."""
+    workgroups (12320 outputs: 770 tiles of 16 in workgroups of 4, or of 5
+    from five token tiles; 8208: 513 tiles in threes; 1296: 81 tiles in
+    fives, the last workgroup one tile) and where the rows fit one workgroup a
+    tile, with one to eight token tiles (twelve, eight and four wavefronts),
+    against the oracle."""
     rng = np.random.default_rng(M * 31 + N)
     x = bf16_rand(rng, (M, K), 0.5)
     w = bf16_rand(rng, (N, K), 0.05)
@@ -434,7 +436,7 @@ def test_project_run_twice_bit_identical(E, decode):
     at the prefill shape)."""
     rng = np.random.default_rng(11)
     w = decode.wkv[1]
-    for T in (1, 3, 8, 64, 300, 4096):
+    for T in (1, 3, 8, 64, 100, 300, 4096):
         x = cuda(bf16_rand(rng, (T, 6144), 0.5))
         ys = []
         for _ in range(2):
