@@ -19,7 +19,9 @@
 // barrier ends every phase, so group 0 (wavefronts 0-3) always runs one
 // phase ahead of group 1 (wavefronts 4-7).  The 256x320 tile is as large as
 // the registers of two wavefronts a SIMD allow.  320 outputs divide 20480,
-// and 4096 x 20480 makes 1024 tiles, four full rounds of 256 CUs.
+// and 4096 x 20480 makes 1024 tiles, four full rounds of 256 CUs.  For a few
+// hundred tokens, whose 256-token tiles would leave CUs idle, the same kernel
+// runs with 128-token tiles (four token blocks a wavefront instead of eight).
 //
 // Data movement: global memory goes straight to LDS (buffer_load ... lds, 1
 // KiB a load, no register staging) into a 4-stage ring of 36 KiB stages, so
@@ -45,7 +47,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256;            // tokens per tile
 constexpr int BN = 320;            // outputs per tile
 constexpr int BK = 32;             // K per stage
 constexpr int KCH = BK / 8;        // 16-byte chunks per tile row (4)
@@ -53,17 +54,23 @@ constexpr int NSTAGE = 4;          // LDS stages
 constexpr int AHEAD = NSTAGE - 1;  // K tiles in flight ahead of the one being read
 constexpr int GROUP_M = 8;         // token tiles walked per wkv tile
 constexpr int XCDS = 8;
-constexpr int TB = 8;              // 16-token MFMA blocks per wavefront (128 tokens)
 constexpr int WB = 5;              // 16-output MFMA blocks per wavefront (80 outputs)
-constexpr int NF = TB + WB;        // operand fragments per wavefront per K tile
-constexpr int LT = BM / 16 / 4;    // 1 KiB token-row loads per group-0 wavefront per stage (4)
 constexpr int LW = BN / 16 / 4;    // 1 KiB wkv-row loads per group-1 wavefront per stage (5)
 
-typedef __attribute__((address_space(3))) void *lptr_t;
+// The token side of a tile, for TB 16-token MFMA blocks per wavefront: 256
+// tokens a tile at TB = 8 (the prefill tile), 128 at TB = 4 (twice the tiles
+// for a few hundred tokens, whose 256-token tiles leave CUs idle).
+template <int TB>
+struct TokenSide {
+    static constexpr int BM = 32 * TB;                 // tokens per tile
+    static constexpr int NF = TB + WB;                 // fragments per wavefront per K tile
+    static constexpr int LT = BM / 16 / 4;             // token-row loads per group-0 wavefront
+    static constexpr int STAGE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per stage
+    static_assert(NSTAGE * STAGE_SLOTS * 16 <= 160 * 1024, "LDS stages");
+    static_assert(LT <= LW, "per-wavefront load offsets sized for the larger share");
+};
 
-constexpr int STAGE_SLOTS = (BM + BN) * KCH;   // 16-byte LDS slots per stage (36 KiB)
-static_assert(NSTAGE * STAGE_SLOTS * 16 <= 160 * 1024, "LDS stages");
-static_assert(LT <= LW, "per-wavefront load offsets sized for the larger share");
+typedef __attribute__((address_space(3))) void *lptr_t;
 
 // LDS position of 16-byte chunk c of tile row r: c ^ swizzle(r).  Among any
 // 16 consecutive rows read at one chunk, the rows that share a 256-byte bank
@@ -91,12 +98,15 @@ __device__ __forceinline__ void phase_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+template <int TB>
 __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ A,
                                                    const uint16_t *__restrict__ B,
                                                    uint16_t *__restrict__ C, int M, int N, int K,
                                                    int tiles_m, int tiles_n)
 {
-    // [stage][256 token rows, then 320 wkv rows][4 chunks]
+    constexpr int BM = TokenSide<TB>::BM, NF = TokenSide<TB>::NF, LT = TokenSide<TB>::LT;
+    constexpr int STAGE_SLOTS = TokenSide<TB>::STAGE_SLOTS;
+    // [stage][BM token rows, then 320 wkv rows][4 chunks]
     __shared__ u32x4 smem[NSTAGE][STAGE_SLOTS];
 
     // ---- tile of this workgroup: XCD-contiguous ranges, grouped raster
@@ -132,10 +142,10 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
     int lbase[LW];
 #pragma unroll
     for (int j = 0; j < LW; j++) {
-        if (grp == 0) {               // token rows 64s .. 64s+63
-            const int row = simd * 64 + 16 * j + lrow;
+        if (grp == 0) {               // token rows (BM/4)s .. (BM/4)s + BM/4-1
+            const int row = simd * (BM / 4) + 16 * j + lrow;
             goff[j] = ((uint32_t)(m0 + row) * K + (lslot ^ swizzle(row)) * 8) * 2;
-            lbase[j] = (simd * 64 + 16 * j) * KCH;
+            lbase[j] = (simd * (BM / 4) + 16 * j) * KCH;
         } else {                      // wkv rows 80s .. 80s+79
             const int row = simd * 80 + 16 * j + lrow;
             goff[j] = ((uint32_t)(n0 + row) * K + (lslot ^ swizzle(row)) * 8) * 2;
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
     auto read_tile = [&](int st) {
 #pragma unroll
         for (int f = 0; f < NF; f++) {
-            const int row = f < WB ? BM + oq * 80 + f * 16 + fr : th * 128 + (f - WB) * 16 + fr;
+            const int row = f < WB ? BM + oq * 80 + f * 16 + fr : th * (BM / 2) + (f - WB) * 16 + fr;
             frag[f] = __builtin_bit_cast(bf16x8, smem[st][row * KCH + (fch ^ swizzle(row))]);
         }
     };
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint16_t *__restrict__ 
     // are all in range or all past it)
 #pragma unroll
     for (int j = 0; j < TB; j++) {
-        const int m = m0 + th * 128 + j * 16 + fr;
+        const int m = m0 + th * (BM / 2) + j * 16 + fr;
         if (m >= M)
             continue;
         uint16_t *crow = C + (int64_t)m * N;
@@ -266,10 +276,21 @@ int32_t launch_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M
 {
     if (M == 0)
         return ENGRAM_OK;
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const int64_t tiles = (int64_t)tiles_m * tiles_n;
-    dispatch(gemm_kernel, dim3((unsigned)tiles), dim3(512), l, true, true, x, w, y, (int)M, (int)N,
-             (int)K, tiles_m, tiles_n);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    // 128-token tiles when 256-token ones would leave CUs idle and the
+    // smaller ones still fit in one round (each output adds the same products
+    // in the same order either way)
+    const int cus = device_cus();
+    const int64_t w8 = ((M + 255) / 256) * tiles_n, w4 = ((M + 127) / 128) * tiles_n;
+    if (w8 < cus && w4 <= cus) {
+        const int tiles_m = (int)((M + 127) / 128);
+        dispatch(gemm_kernel<4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), l, true, true,
+                 x, w, y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+    } else {
+        const int tiles_m = (int)((M + 255) / 256);
+        dispatch(gemm_kernel<8>, dim3((unsigned)((int64_t)tiles_m * tiles_n)), dim3(512), l, true,
+                 true, x, w, y, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+    }
     return launch_status("engram gemm kernel");
 }
 

@@ -414,6 +414,26 @@ def test_project_gemm_full_shape(E, decode, M):
     check_project(E, x, decode.wkv[1], decode.layers[1]["wkv"], rows, cols)
 
 
+def test_project_gemm_token_tiles_agree(E, decode):
+    """A few hundred tokens take 128-token tiles, more take 256-token ones;
+    each output adds the same products in the same order either way, so 300
+    tokens alone equal the same 300 tokens inside a 1100-token call bit for
+    bit (and the oracle within the projection tolerance, on sampled rows)."""
+    import oracle
+    rng = np.random.default_rng(4242)
+    ids = rng.integers(0, decode.layers[0]["rows"], size=(1100, 24))
+    x = decode.oracle_rows(0, ids).reshape(1100, -1)
+    big = torch.empty(1100, 20480, dtype=torch.int16, device="cuda")
+    small = torch.empty(300, 20480, dtype=torch.int16, device="cuda")
+    log("project: 300 tokens (128-token tiles) vs 1100 tokens (256-token tiles)")
+    E.project(cuda(x), decode.wkv[0], big)
+    E.project(cuda(x[400:700]), decode.wkv[0], small)
+    np.testing.assert_array_equal(to_np_u16(small), to_np_u16(big)[400:700])
+    rows = np.array([0, 127, 128, 255, 256, 299])
+    want = oracle.linear_bf16(x[400:700][rows], decode.layers[0]["wkv"])
+    assert relerr(widen(to_np_u16(small)[rows]), widen(want)) <= 1e-2
+
+
 @pytest.mark.parametrize("M", [300, 1000, 4133])
 def test_project_gemm_ragged_full_k(E, decode, M):
     """Token counts that leave a partly filled last 256-token tile, at the
