@@ -130,7 +130,8 @@ int32_t check_table(const engram_table *tab)
           (long long)tab->n_rows, (const void *)tab->d_data);
     if (tab->fmt == ENGRAM_FMT_Q2K) {
         CHECK(tab->head_dim == 256, ENGRAM_E_UNSUPPORTED,
-              "engram rows are one Q2_K block: head_dim must be 256, got %d", tab->head_dim);
+              "engram Q2_K table: a row is one 256-value block, so head_dim is 256 (got %d)",
+              tab->head_dim);
         CHECK(aligned(tab->d_data, 4), ENGRAM_E_ARG, "engram Q2_K table must be 4-byte aligned");
     } else if (tab->fmt == ENGRAM_FMT_E4M3) {
         CHECK(tab->head_dim >= 16 && tab->head_dim <= 1024 && tab->head_dim % 16 == 0,
@@ -210,8 +211,8 @@ int32_t check_gate(const float *h, const uint16_t *kv, const float *qk, int64_t 
                    int64_t dim, float eps)
 {
     CHECK(T >= 0, ENGRAM_E_ARG, "engram gate: T = %lld", (long long)T);
-    CHECK(hc >= 1 && hc <= 4, ENGRAM_E_UNSUPPORTED, "engram gate supports hc_mult 1..=4, got %d",
-          hc);
+    CHECK(hc >= 1 && hc <= 4, ENGRAM_E_UNSUPPORTED,
+          "engram gate: %d hyper-connection streams, 1 to 4 supported", hc);
     CHECK(dim >= 256 && dim % 256 == 0 && dim <= (1 << 20), ENGRAM_E_UNSUPPORTED,
           "engram gate: dim = %lld must be a multiple of 256", (long long)dim);
     CHECK(std::isfinite(eps) && eps >= 0.0f, ENGRAM_E_ARG, "engram gate: eps = %g", (double)eps);
@@ -630,7 +631,7 @@ int32_t engram_ctx_create(const engram_config *cfg, void *d_workspace, size_t wo
     if (rc != ENGRAM_OK)
         return rc;
     CHECK(cfg->hc >= 1 && cfg->hc <= 4, ENGRAM_E_UNSUPPORTED,
-          "engram gate supports hc_mult 1..=4, got %d", cfg->hc);
+          "engram gate: %d hyper-connection streams, 1 to 4 supported", cfg->hc);
     CHECK(cfg->dim >= 256 && cfg->dim % 256 == 0, ENGRAM_E_UNSUPPORTED,
           "engram dim %lld must be a multiple of 256", (long long)cfg->dim);
     CHECK(cfg->head_dim >= 16 && cfg->head_dim % 16 == 0 && cfg->head_dim <= 1024,

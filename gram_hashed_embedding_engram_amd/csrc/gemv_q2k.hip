@@ -1,6 +1,6 @@
 // Stage 3 at one token with wkv shipped as Q2_K blocks (atlascybernetics
-// "spark_model/layers/engram_v41.rs", EngramLayerWeights::wkv_q2k, read by
-// the single-token projection in place of the bf16 expansion).
+// "spark_model/layers/engram_v41.rs", EngramLayerWeights::wkv_q2k: one
+// token's projection reads these blocks instead of their bf16 expansion).
 //
 // y[n] = bf16(sum_k x[k] * w[n][k]) with w[n][k] the bf16 weight its Q2_K
 // block decodes to.  Persistent wavefronts (two 1024-thread workgroups per

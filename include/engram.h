@@ -1,11 +1,11 @@
 /*
  * engram.h -- C ABI of the MI355X (gfx950) engram hot path.
  *
- * The DeepSeek-V4.1 engram layer, per token: hash the n-gram window of
- * compressed token ids into `cols` table row ids, gather and dequantise those
- * rows to bf16, project their concatenation through `wkv` into one key per
- * hyper-connection stream plus one shared value, and gate the value onto the
- * FP32 highway (atlascybernetics "spark_model/layers/engram_v41.rs", module
+ * The DeepSeek-V4.1 engram layer, per token: hash the token's window of the
+ * last max_ngram compressed ids into `cols` table row ids, gather and
+ * dequantise those rows to bf16, project their concatenation through `wkv`
+ * into a key for each hyper-connection stream and a value the streams share,
+ * and gate the value onto the FP32 highway (atlascybernetics "spark_model/layers/engram_v41.rs", module
  * doc, stages 1-4; metrale "metrale_model_arch/deepseek_v41_ref/engram.rs",
  * module doc).
  *

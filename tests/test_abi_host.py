@@ -126,7 +126,7 @@ def test_stream_read_refusals(L):
 def test_gather_refusals(L):
     t = E.TableC(E.FMT_Q2K, 128, 0, 0, 100, FAKE, None)
     rc, msg = rc_msg(L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None, None))
-    assert rc == E.E_UNSUPPORTED and "head_dim must be 256" in msg
+    assert rc == E.E_UNSUPPORTED and "head_dim is 256 (got 128)" in msg
     t = E.TableC(E.FMT_Q2K, 256, 0, 0, 100, FAKE + 2, None)
     assert L.engram_gather_dequant(ctypes.byref(t), FAKE, 4, 24, 48, FAKE, None, None) == E.E_ARG
     t = E.TableC(E.FMT_E4M3, 256, 100, 0, 100, FAKE, FAKE)
