@@ -39,8 +39,8 @@ def brute_force(token_map, pad_id, mult, primes, offsets, ids, start_pos=0, hist
         p = start_pos + s
         window = []
         for k in range(ng):
-            # pad from the first shift that reaches before position 0 or
-            # lands on an unmapped id, through every larger shift
+            # shift k reads the pad id when any shift up to k falls before
+            # the sequence start or finds an unmapped id
             blocked = any(p - j < 0 or comp.get(p - j, 0) == -1 for j in range(k + 1))
             window.append(pad_id if blocked else comp.get(p - k, 0))
         per_layer = []
